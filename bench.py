@@ -1,0 +1,256 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = sparse_attn_plan (pool, scores, hybrid top-k/top-p select, CSR) followed by
+sparse_attn_fwd over the kept tiles, on seeded synthetic video-token Q, K, V already
+resident in HBM. Prints one JSON line:
+
+  value        effective TFLOP/s over the exact kept query-key pairs (4*D flops per
+               pair) per step, plan included
+  roofline     the forward kernel (the dominant one): kept-pair flops / its average
+               duration from HIP events on the launch stream, against the bf16 MFMA peak
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same workload
+
+plus the dense-mask run of the same kernel (speedup and per-kept-tile utilisation).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14b_720p]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "sparse-attn ms/call + effective TFLOP/s (kept tiles) vs bf16 MFMA peak @90/95%"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "attention.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kept_flops(rp: np.ndarray, ci: np.ndarray, w: W.Workload) -> float:
+    """4*D flops per kept (query, key) pair, ragged blocks counted by real tokens."""
+    nq = w.n_qblk
+    qsize = np.minimum(w.block_q, w.N - np.arange(nq) * w.block_q).astype(np.int64)
+    ksize = np.minimum(w.block_kv, w.N - np.arange(w.n_kvblk) * w.block_kv).astype(np.int64)
+    counts = np.diff(rp)
+    rows_q = np.tile(qsize, w.B * w.H)
+    pairs = int(np.sum(np.repeat(rows_q, counts) * ksize[ci]))
+    return 4.0 * w.D * pairs, pairs
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str, launch_bytes_alg: float):
+    """HBM bytes per forward launch from committed rocprofv3 counters, when they were
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(workload)
+    if not ent or ent.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 20.0):
+    """The oracle as it stands, on a bounded sample: the mask track of one head and the
+    float64 output track of query blocks of that head until the budget is used."""
+    from oracle import oracle_plan, sparse_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q32 = W.to_f32(q[:, :1])
+    k32 = W.to_f32(k[:, :1])
+    v32 = W.to_f32(v[:, :1])
+    t0 = time.perf_counter()
+    oracle_plan(q32, k32, w.block_q, w.block_kv, w.topk, w.top_p, rows=[(0, 0, 0)])
+    t_mask = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.n_qblk)
+    done_flops, n_rows, t1 = 0.0, 0, time.perf_counter()
+    ksize = np.minimum(w.block_kv, w.N - np.arange(w.n_kvblk) * w.block_kv)
+    wh = w.replace(H=1)
+    for I in order:
+        I = int(I)
+        sparse_attention(q32, k32, v32, rp[: w.n_qblk + 1], ci, w.block_q, w.block_kv,
+                         rows=[(0, 0, I)])
+        qs = min(w.block_q, w.N - I * w.block_q)
+        done_flops += 4.0 * w.D * qs * float(ksize[ci[rp[I]:rp[I + 1]]].sum())
+        n_rows += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_out = time.perf_counter() - t1
+    return {
+        "value": done_flops / t_out / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.name}: float64 sparse output track over {n_rows} of "
+                   f"{w.n_qblk} query blocks ({t_out:.1f} s); the mask track for one query "
+                   f"block of that head took {t_mask:.2f} s (pooling of the whole head included)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p", choices=sorted(W.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_05_amd as sa
+
+    w = W.CONFIGS[args.workload]
+    t0 = time.time()
+    q, k, v, alpha = W.make_inputs(w)
+    log(f"inputs {w.name}: B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype} in {time.time() - t0:.1f}s")
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    dq, dk, dv = dev(q), dev(k), dev(v)
+    dalpha = dev(alpha) if w.linear else None
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(sa.plan_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(dq)
+
+    def step():
+        p = sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        ev_mid.record(stream)
+        sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
+        return p
+
+    ev_mid = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        p = step()
+    torch.cuda.synchronize()
+    rp, ci = p.csr()
+    flops, pairs = kept_flops(rp, ci, w)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        p = sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        mids[i].record(stream)
+        sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_plan = [s.elapsed_time(m) for s, m in zip(starts, mids)]
+    ms_fwd = [m.elapsed_time(e) for m, e in zip(mids, ends)]
+    t_step = float(np.mean(ms_step))
+    t_fwd = float(np.mean(ms_fwd))
+    t_plan = float(np.mean(ms_plan))
+    log(f"step {t_step:.3f} ms (plan {t_plan:.3f}, fwd {t_fwd:.3f}); wall {1e3 * wall / args.steps:.3f} ms/step")
+
+    res_extra = {}
+    if not args.no_dense:
+        pd = sa.plan_dense(dq, w.block_q, w.block_kv)
+        for _ in range(max(1, args.warmup)):
+            sa.fwd(dq, dk, dv, pd, out=o)
+        nd = max(3, min(args.steps, 10))
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+        for i in range(nd):
+            e0[i].record(stream)
+            sa.fwd(dq, dk, dv, pd, out=o)
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        t_dense = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
+        dflops = 4.0 * w.D * w.B * w.H * float(w.N) * w.N
+        res_extra = {
+            "ms_dense_fwd": round(t_dense, 4),
+            "dense_tflops": round(dflops / t_dense / 1e9, 2),
+            "speedup_vs_dense": round(t_dense / t_step, 3),
+            "speedup_vs_dense_fwd_only": round(t_dense / t_fwd, 3),
+            "per_kept_tile_util_ratio": round((flops / t_fwd) / (dflops / t_dense), 4),
+        }
+        del pd
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops / t_fwd / 1e9
+    eb = w.elem_bytes
+    alg_bytes = 4.0 * w.B * w.H * w.N * w.D * eb + 4.0 * (w.rows + 1 + len(ci))
+    traffic = traffic_for(w.name, alg_bytes)
+    nnz = int(rp[-1])
+    out = {
+        "metric": METRIC,
+        "value": round(flops / t_step / 1e9, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "grid": list(w.grid),
+            "block_q": w.block_q, "block_kv": w.block_kv, "topk": w.topk, "top_p": w.top_p,
+            "linear_branch": bool(w.linear),
+        },
+        "ms_plan": round(t_plan, 4),
+        "ms_fwd": round(t_fwd, 4),
+        "fwd_tflops": round(achieved, 2),
+        "kept_pairs": pairs,
+        "nnz_tiles": nnz,
+        "tile_sparsity": round(1.0 - nnz / float(w.rows * w.n_kvblk), 5),
+        "pair_sparsity": round(1.0 - pairs / float(w.B * w.H * w.N * w.N), 5),
+        **res_extra,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel": "sparse_fwd_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp, ci)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,19 @@
+"""Block-sparse softmax attention for video DiTs on MI355X (gfx950).
+
+Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
+
+    plan(q, k, block_q, block_kv, topk, top_p)  the hybrid top-k / top-p block router
+    fwd(q, k, v, plan, alpha=None)              attention over the kept tiles, with the
+                                                optional elu+1 linear branch blend
+    plan_dense(q, ...), plan_from_csr(q, ...)   all-ones and caller-given masks
+
+All computation happens in the library's HIP kernels; torch supplies device memory and
+streams.
+"""
+from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, fwd, load_library,
+                       plan, plan_dense, plan_from_csr, plan_workspace_bytes, router_exp, version)
+
+__all__ = [
+    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "fwd", "load_library",
+    "plan", "plan_dense", "plan_from_csr", "plan_workspace_bytes", "router_exp", "version",
+]

@@ -1,0 +1,276 @@
+"""ctypes binding of libsparse_attn.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module checks
+tensor shapes, allocates workspaces with torch (device memory and streams are all torch
+provides here) and passes raw pointers and sizes across the C ABI declared in
+include/sparse_attn.h. When the library is missing, every entry point raises; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SPARSE_ATTN_LIB", os.path.join(HERE, "libsparse_attn.so"))
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE = 0, -1, -2, -3
+SA_ERR_PLAN_MISMATCH, SA_ERR_BAD_CSR, SA_ERR_HIP = -4, -5, -6
+SA_BF16, SA_FP32 = 0, 1
+
+EXPORTS = (
+    "sparse_attn_plan_workspace_bytes", "sparse_attn_plan", "sparse_attn_plan_dense",
+    "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
+    "sparse_attn_router_exp", "sparse_attn_status_string", "sparse_attn_version",
+)
+
+
+class SaPlan(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+        ("n_qblk", ctypes.c_int32), ("n_kvblk", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("row_order", ctypes.c_void_p),
+    ]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads the HIP library once; raises when it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found: build it with `python -m block_sparse_attention_05_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    pplan = ctypes.POINTER(SaPlan)
+    lib.sparse_attn_plan_workspace_bytes.argtypes = [i32] * 6
+    lib.sparse_attn_plan_workspace_bytes.restype = sz
+    lib.sparse_attn_plan.argtypes = [vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, sz, pplan, vp]
+    lib.sparse_attn_plan.restype = i32
+    lib.sparse_attn_plan_dense.argtypes = [i32] * 7 + [vp, sz, pplan, vp]
+    lib.sparse_attn_plan_dense.restype = i32
+    lib.sparse_attn_plan_from_csr.argtypes = [i32] * 7 + [vp, vp, vp, sz, pplan, vp]
+    lib.sparse_attn_plan_from_csr.restype = i32
+    lib.sparse_attn_fwd_workspace_bytes.argtypes = [i32] * 5
+    lib.sparse_attn_fwd_workspace_bytes.restype = sz
+    lib.sparse_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_fwd.restype = i32
+    lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
+    lib.sparse_attn_router_exp.restype = i32
+    lib.sparse_attn_status_string.argtypes = [i32]
+    lib.sparse_attn_status_string.restype = ctypes.c_char_p
+    lib.sparse_attn_version.argtypes = []
+    lib.sparse_attn_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _status_string(st: int) -> str:
+    try:
+        return load_library().sparse_attn_status_string(st).decode()
+    except Exception:  # the library itself is missing
+        return "unknown"
+
+
+def _check(st: int, what: str) -> None:
+    if st != SA_OK:
+        raise SparseAttnError(st, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check_qkv(*ts):
+    t0 = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, D]")
+        if t.dim() != 4 or tuple(t.shape) != tuple(t0.shape) or t.dtype != t0.dtype:
+            raise ValueError("q, k, v must share one [B, H, N, D] shape and one dtype")
+        if t.device != t0.device:
+            raise ValueError("tensors must be on one device")
+
+
+class Plan:
+    """A block mask in CSR form living in a torch-owned workspace on the GPU."""
+
+    def __init__(self, ws, st: SaPlan):
+        self.ws = ws          # keeps the workspace (and so the CSR arrays) alive
+        self.st = st
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int]:
+        return (self.st.B, self.st.H, self.st.N, self.st.D)
+
+    @property
+    def blocks(self) -> Tuple[int, int]:
+        return (self.st.block_q, self.st.block_kv)
+
+    @property
+    def rows(self) -> int:
+        return self.st.B * self.st.H * self.st.n_qblk
+
+    def _view(self, ptr: int, count: int):
+        torch = _torch()
+        off = ptr - self.ws.data_ptr()
+        return self.ws[off:off + 4 * count].view(torch.int32)
+
+    def row_ptr(self):
+        return self._view(self.st.row_ptr, self.rows + 1)
+
+    def col_idx(self, nnz: Optional[int] = None):
+        if nnz is None:
+            nnz = int(self.row_ptr()[-1].item())
+        return self._view(self.st.col_idx, nnz)
+
+    def row_order(self):
+        return self._view(self.st.row_order, self.rows)
+
+    def csr(self) -> Tuple[np.ndarray, np.ndarray]:
+        """(row_ptr, col_idx) copied to host numpy arrays (synchronises)."""
+        rp = self.row_ptr().cpu().numpy().astype(np.int64)
+        ci = self.col_idx(int(rp[-1])).cpu().numpy()
+        return rp, ci
+
+
+def _new_ws(nbytes: int, device):
+    torch = _torch()
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws
+
+
+def plan_workspace_bytes(B, H, N, D, block_q, block_kv) -> int:
+    return int(load_library().sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv))
+
+
+def plan(q, k, block_q: int = 128, block_kv: int = 64, topk: float = 0.05, top_p: float = 0.9,
+         stream=None, workspace=None) -> Plan:
+    """The hybrid top-k / top-p block mask of q, k [B, H, N, D] (see sparse_attn_plan)."""
+    lib = load_library()
+    _check_qkv(q, k)
+    B, H, N, D = q.shape
+    need = lib.sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "plan shape")
+    ws = workspace if workspace is not None else _new_ws(need, q.device)
+    st = SaPlan()
+    _check(lib.sparse_attn_plan(q.data_ptr(), k.data_ptr(), _dtype_code(q), B, H, N, D, block_q,
+                                block_kv, float(topk), float(top_p), ws.data_ptr(), ws.numel(),
+                                ctypes.byref(st), _stream(stream)), "sparse_attn_plan")
+    return Plan(ws, st)
+
+
+def plan_dense(q, block_q: int = 128, block_kv: int = 64, stream=None) -> Plan:
+    """The all-ones mask for q's shape (dense attention through the sparse kernel)."""
+    lib = load_library()
+    B, H, N, D = q.shape
+    need = lib.sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "plan shape")
+    ws = _new_ws(need, q.device)
+    st = SaPlan()
+    _check(lib.sparse_attn_plan_dense(_dtype_code(q), B, H, N, D, block_q, block_kv, ws.data_ptr(),
+                                      ws.numel(), ctypes.byref(st), _stream(stream)),
+           "sparse_attn_plan_dense")
+    return Plan(ws, st)
+
+
+def plan_from_csr(q, row_ptr: np.ndarray, col_idx: np.ndarray, block_q: int = 128,
+                  block_kv: int = 64, stream=None) -> Plan:
+    """A caller-given CSR mask (host arrays), validated and copied to the GPU."""
+    lib = load_library()
+    B, H, N, D = q.shape
+    need = lib.sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "plan shape")
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    ws = _new_ws(need, q.device)
+    st = SaPlan()
+    _check(lib.sparse_attn_plan_from_csr(_dtype_code(q), B, H, N, D, block_q, block_kv,
+                                         rp.ctypes.data, ci.ctypes.data if ci.size else None,
+                                         ws.data_ptr(), ws.numel(), ctypes.byref(st),
+                                         _stream(stream)), "sparse_attn_plan_from_csr")
+    return Plan(ws, st)
+
+
+def fwd(q, k, v, plan: Plan, alpha=None, return_lse: bool = False, out=None, lse=None,
+        workspace=None, stream=None):
+    """Block-sparse attention over plan's kept tiles, optionally blended with the linear
+    branch (see sparse_attn_fwd). Returns o, or (o, lse) with return_lse."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    if alpha is not None:
+        if not (alpha.is_cuda and alpha.dtype == torch.float32 and alpha.is_contiguous()
+                and tuple(alpha.shape) == (H, D)):
+            raise ValueError("alpha must be a contiguous float32 [H, D] GPU tensor")
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = lib.sparse_attn_fwd_workspace_bytes(B, H, N, D, 1 if alpha is not None else 0)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = _new_ws(need, q.device)
+    _check(lib.sparse_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, N, D,
+                               ctypes.byref(plan.st),
+                               alpha.data_ptr() if alpha is not None else None, o.data_ptr(),
+                               lse.data_ptr() if lse is not None else None,
+                               ws.data_ptr() if ws is not None else None,
+                               ws.numel() if ws is not None else 0, _stream(stream)),
+           "sparse_attn_fwd")
+    return (o, lse) if return_lse else o
+
+
+def router_exp(x, stream=None):
+    """The router's device exp over a float32 GPU tensor (diagnostic)."""
+    torch = _torch()
+    lib = load_library()
+    if not (x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()):
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    y = torch.empty_like(x)
+    _check(lib.sparse_attn_router_exp(x.data_ptr(), y.data_ptr(), x.numel(), _stream(stream)),
+           "sparse_attn_router_exp")
+    return y
+
+
+def version() -> int:
+    return int(load_library().sparse_attn_version())

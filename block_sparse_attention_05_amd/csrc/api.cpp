@@ -1,0 +1,305 @@
+// C ABI of the block-sparse attention library: argument validation, workspace layout
+// and kernel launches. Every check runs on the host before the first launch.
+
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "sa_internal.h"
+
+using namespace sa;
+
+namespace {
+
+struct Shape {
+  int B, H, N, D, bq, bk, nQ, nKV;
+  long R;
+};
+
+sa_status check_shape(int B, int H, int N, int D, int bq, int bk, Shape *sh) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || bq <= 0 || bk <= 0) return SA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SA_ERR_UNSUPPORTED;
+  if (bq != 64 && bq != 128) return SA_ERR_UNSUPPORTED;
+  if (bk != 64) return SA_ERR_UNSUPPORTED;
+  const int nQ = ceil_div(N, bq), nKV = ceil_div(N, bk);
+  if (nKV > kMaxKvBlocks) return SA_ERR_UNSUPPORTED;
+  const long R = (long)B * H * nQ;
+  if (R * (long)nKV >= (1L << 31)) return SA_ERR_UNSUPPORTED;
+  if ((long)B * H > 65535) return SA_ERR_UNSUPPORTED;
+  *sh = Shape{B, H, N, D, bq, bk, nQ, nKV, R};
+  return SA_OK;
+}
+
+bool dtype_ok(int dt) { return dt == SA_BF16 || dt == SA_FP32; }
+
+// Plan workspace layout (each piece 256-byte aligned).
+struct PlanLayout {
+  size_t row_ptr, col_idx, row_order, counts, bitmap, qbar, kbar, scores, total;
+};
+
+PlanLayout plan_layout(const Shape &s) {
+  PlanLayout L;
+  const size_t nwords = (size_t)ceil_div(s.nKV, 32);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.row_ptr = take((size_t)(s.R + 1) * 4);
+  L.col_idx = take((size_t)s.R * s.nKV * 4);
+  L.row_order = take((size_t)s.R * 4);
+  L.counts = take((size_t)s.R * 4);
+  L.bitmap = take((size_t)s.R * nwords * 4);
+  L.qbar = take((size_t)s.B * s.H * s.nQ * s.D * 4);
+  L.kbar = take((size_t)s.B * s.H * s.nKV * s.D * 4);
+  L.scores = take((size_t)s.B * s.H * s.nQ * s.nKV * 4);
+  L.total = off;
+  return L;
+}
+
+sa_status check_ws(const void *ws, size_t have, size_t need) {
+  if (need == 0) return SA_OK;
+  if (ws == nullptr || have < need) return SA_ERR_WORKSPACE;
+  if (((uintptr_t)ws) % kAlign != 0) return SA_ERR_WORKSPACE;
+  return SA_OK;
+}
+
+void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L) {
+  p->B = s.B;
+  p->H = s.H;
+  p->N = s.N;
+  p->D = s.D;
+  p->block_q = s.bq;
+  p->block_kv = s.bk;
+  p->n_qblk = s.nQ;
+  p->n_kvblk = s.nKV;
+  p->dtype = dt;
+  p->reserved = 0;
+  p->row_ptr = reinterpret_cast<int32_t *>(ws + L.row_ptr);
+  p->col_idx = reinterpret_cast<int32_t *>(ws + L.col_idx);
+  p->row_order = reinterpret_cast<int32_t *>(ws + L.row_order);
+}
+
+sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+// Linear-branch workspace: per head sum_j phi(k_j) v_j^T [D, D], sum_j phi(k_j) [D], and
+// per-chunk partials of both.
+struct FwdLayout {
+  size_t lin_h, lin_z, partial, total;
+  int chunks;
+};
+
+FwdLayout fwd_layout(const Shape &s, int with_linear) {
+  FwdLayout L{0, 0, 0, 0, 0};
+  if (!with_linear) return L;
+  const size_t BH = (size_t)s.B * s.H;
+  L.chunks = linear_prepass_chunks(s.N);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.lin_h = take(BH * s.D * s.D * 4);
+  L.lin_z = take(BH * s.D * 4);
+  L.partial = take(BH * (size_t)L.chunks * s.D * (s.D + 1) * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_attn_plan_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv) {
+  Shape s;
+  if (check_shape(B, H, N, D, block_q, block_kv, &s) != SA_OK) return 0;
+  return plan_layout(s).total;
+}
+
+sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, int H, int N,
+                           int D, int block_q, int block_kv, double topk_frac, double top_p,
+                           void *workspace, size_t ws_bytes, sa_plan *out, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || out == nullptr) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  if (!(topk_frac >= 0.0 && topk_frac <= 1.0)) return SA_ERR_INVALID_ARG;
+  if (!(top_p >= 0.0 && top_p <= 1.0)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
+  if (st != SA_OK) return st;
+  const PlanLayout L = plan_layout(s);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != SA_OK) return st;
+
+  // top-k count and the fp32 threshold factor, fixed on the host in one place
+  double mk = ceil(topk_frac * (double)s.nKV - 1e-9);
+  if (mk < 1.0) mk = 1.0;
+  if (mk > s.nKV) mk = s.nKV;
+  const int m_k = (int)mk;
+  const float p32 = (float)top_p;
+  const int p_all = top_p >= 1.0 ? 1 : 0;
+  const float c = (float)(1.0 / sqrt((double)D));
+
+  char *ws = static_cast<char *>(workspace);
+  float *qbar = reinterpret_cast<float *>(ws + L.qbar);
+  float *kbar = reinterpret_cast<float *>(ws + L.kbar);
+  float *scores = reinterpret_cast<float *>(ws + L.scores);
+  uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + L.bitmap);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
+  sa_plan p;
+  fill_plan(&p, s, dtype, ws, L);
+  const int BH = B * H;
+  const int nwords = ceil_div(s.nKV, 32);
+
+  hipError_t e = launch_pool(q, dtype, BH, N, D, block_q, qbar, stream);
+  if (e == hipSuccess) e = launch_pool(k, dtype, BH, N, D, block_kv, kbar, stream);
+  if (e == hipSuccess) e = launch_scores(qbar, kbar, BH, s.nQ, s.nKV, D, c, scores, stream);
+  if (e == hipSuccess)
+    e = launch_select(scores, (int)s.R, s.nKV, m_k, p32, p_all, bitmap, nwords, counts, stream);
+  if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, stream);
+  if (e == hipSuccess) e = launch_fill(bitmap, nwords, p.row_ptr, (int)s.R, p.col_idx, stream);
+  if (e == hipSuccess)
+    e = launch_row_order(p.row_ptr, (int)s.R, s.nKV, p.row_order, counts, stream);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  *out = p;
+  return SA_OK;
+}
+
+sa_status sparse_attn_plan_dense(sa_dtype dtype, int B, int H, int N, int D, int block_q,
+                                 int block_kv, void *workspace, size_t ws_bytes, sa_plan *out,
+                                 hipStream_t stream) {
+  if (out == nullptr || !dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
+  if (st != SA_OK) return st;
+  const PlanLayout L = plan_layout(s);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != SA_OK) return st;
+  sa_plan p;
+  fill_plan(&p, s, dtype, static_cast<char *>(workspace), L);
+  hipError_t e = launch_dense_plan((int)s.R, s.nKV, p.row_ptr, p.col_idx, stream);
+  if (e == hipSuccess)
+    e = launch_row_order(p.row_ptr, (int)s.R, s.nKV, p.row_order,
+                         reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + L.counts),
+                         stream);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  *out = p;
+  return SA_OK;
+}
+
+sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, int block_q,
+                                    int block_kv, const int32_t *host_row_ptr,
+                                    const int32_t *host_col_idx, void *workspace,
+                                    size_t ws_bytes, sa_plan *out, hipStream_t stream) {
+  if (out == nullptr || host_row_ptr == nullptr || !dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
+  if (st != SA_OK) return st;
+  const PlanLayout L = plan_layout(s);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != SA_OK) return st;
+  // validate the caller's CSR
+  if (host_row_ptr[0] != 0) return SA_ERR_BAD_CSR;
+  for (long r = 0; r < s.R; ++r) {
+    const int32_t a = host_row_ptr[r], b = host_row_ptr[r + 1];
+    if (b < a || b - a > s.nKV) return SA_ERR_BAD_CSR;
+  }
+  const long nnz = host_row_ptr[s.R];
+  if (nnz > 0 && host_col_idx == nullptr) return SA_ERR_INVALID_ARG;
+  for (long r = 0; r < s.R; ++r) {
+    for (int32_t i = host_row_ptr[r]; i < host_row_ptr[r + 1]; ++i) {
+      const int32_t c = host_col_idx[i];
+      if (c < 0 || c >= s.nKV) return SA_ERR_BAD_CSR;
+      if (i > host_row_ptr[r] && c <= host_col_idx[i - 1]) return SA_ERR_BAD_CSR;
+    }
+  }
+  sa_plan p;
+  char *ws = static_cast<char *>(workspace);
+  fill_plan(&p, s, dtype, ws, L);
+  hipError_t e = hipMemcpyAsync(p.row_ptr, host_row_ptr, (size_t)(s.R + 1) * 4,
+                                hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess && nnz > 0)
+    e = hipMemcpyAsync(p.col_idx, host_col_idx, (size_t)nnz * 4, hipMemcpyHostToDevice, stream);
+  // the host arrays may be pageable and reused as soon as this call returns
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess)
+    e = launch_row_order(p.row_ptr, (int)s.R, s.nKV, p.row_order,
+                         reinterpret_cast<int32_t *>(ws + L.counts), stream);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  *out = p;
+  return SA_OK;
+}
+
+size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_linear) {
+  Shape s;
+  if (check_shape(B, H, N, D, 64, 64, &s) != SA_OK) return 0;
+  return fwd_layout(s, with_linear).total;
+}
+
+sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype dtype, int B,
+                          int H, int N, int D, const sa_plan *plan, const float *alpha, void *o,
+                          float *lse, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || plan == nullptr)
+    return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, plan->block_q, plan->block_kv, &s);
+  if (st != SA_OK) return st;
+  if (plan->B != B || plan->H != H || plan->N != N || plan->D != D || plan->dtype != dtype ||
+      plan->n_qblk != s.nQ || plan->n_kvblk != s.nKV)
+    return SA_ERR_PLAN_MISMATCH;
+  if (plan->row_ptr == nullptr || plan->col_idx == nullptr) return SA_ERR_INVALID_ARG;
+  const FwdLayout L = fwd_layout(s, alpha != nullptr);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != SA_OK) return st;
+  if (alpha != nullptr) return SA_ERR_UNSUPPORTED;  // linear branch not built yet
+
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.row_ptr = plan->row_ptr;
+  a.col_idx = plan->col_idx;
+  a.row_order = plan->row_order;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.block_q = s.bq;
+  a.block_kv = s.bk;
+  a.n_qblk = s.nQ;
+  a.n_kvblk = s.nKV;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  a.scale_log2_f64 = 1.4426950408889634 / sqrt((double)D);
+  a.alpha = nullptr;
+  a.lin_h = nullptr;
+  a.lin_z = nullptr;
+  return hip_status(launch_fwd(a, dtype, stream));
+}
+
+sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (x == nullptr || y == nullptr))) return SA_ERR_INVALID_ARG;
+  if (n == 0) return SA_OK;
+  return hip_status(launch_router_exp(x, y, n, stream));
+}
+
+const char *sparse_attn_status_string(sa_status status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case SA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SA_ERR_PLAN_MISMATCH: return "plan does not match the inputs";
+    case SA_ERR_BAD_CSR: return "malformed CSR mask";
+    case SA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int sparse_attn_version(void) { return 100; }
+
+}  // extern "C"

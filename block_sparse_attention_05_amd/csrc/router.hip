@@ -1,0 +1,507 @@
+// Block-mask router for gfx950: mean pooling, pooled block scores, the hybrid
+// top-k / top-p selection and the CSR build.
+//
+// The mask must be exactly reproducible, so every fp32 operation here is a separately
+// rounded IEEE operation in one fixed order (this file is compiled with contraction
+// off and the pragma below repeats it):
+//   pool    acc = 0, acc += x_t over the block's tokens in ascending order, mean =
+//           acc / count (correctly rounded division); a ragged last block averages its
+//           real tokens.
+//   score   acc = 0, acc += qbar[d]*kbar[d] for d ascending (product rounded first),
+//           S = acc * fp32(1/sqrt(D)).
+//   order   scores descending, ties to the lower block index (-0 equals +0).
+//   softmax e_J = exp_sa(S_J - S_max) with the own exp below; Z = pairwise tree sum of
+//           e_J in block order (adjacent pairs, zero padding to a power of two).
+//   top-p   thr = fp32(p) * Z; running sum in score order, one add at a time; m_p is
+//           the first prefix length whose sum reaches thr (every block when p >= 1 or
+//           no prefix reaches thr).
+//   union   both rules are prefixes of the same order, so a row keeps the first
+//           max(m_k, m_p) blocks of it (SpargeAttention2 page, section 2(1)).
+// Pooling per block and per head follows the SLA2 page, router item 1.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace sa {
+namespace {
+
+// ---------------------------------------------------------------- fp32 exp
+// exp(x) for x <= 0 from rounded fp32 operations only: Cody-Waite reduction with ln 2 =
+// C1 + C2 (C1 has 16 significant bits so n*C1 is exact), a degree-7 Taylor polynomial
+// in Horner form on |r| <= ln(2)/2, and exact scaling by 2^n. Arguments below -86
+// return 0, so every nonzero result is a normal number.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2Hi = 0.693145751953125f;
+constexpr float kLn2Lo = (float)(0.6931471805599453094 - 0.693145751953125);
+constexpr float kC0 = 1.0f;
+constexpr float kC1 = 1.0f;
+constexpr float kC2 = (float)(1.0 / 2.0);
+constexpr float kC3 = (float)(1.0 / 6.0);
+constexpr float kC4 = (float)(1.0 / 24.0);
+constexpr float kC5 = (float)(1.0 / 120.0);
+constexpr float kC6 = (float)(1.0 / 720.0);
+constexpr float kC7 = (float)(1.0 / 5040.0);
+
+__device__ __forceinline__ float exp_sa(float x) {
+  if (!(x >= -86.0f)) return 0.0f;
+  const float n = __builtin_rintf(x * kLog2e);
+  const float r = (x - n * kLn2Hi) - n * kLn2Lo;
+  float p = kC7;
+  p = p * r + kC6;
+  p = p * r + kC5;
+  p = p * r + kC4;
+  p = p * r + kC3;
+  p = p * r + kC2;
+  p = p * r + kC1;
+  p = p * r + kC0;
+  return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// ---------------------------------------------------------------- pooling
+// One thread owns 8 channels of one block and walks its tokens in order; D/8 threads
+// cover a block row, so each token row is read as contiguous 16-byte pieces.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int N, int bs,
+                                                   int nblk, long total_blocks,
+                                                   float *__restrict__ out) {
+  constexpr int kTpb = D / 8;
+  constexpr int kBlocksPerWg = 256 / kTpb;
+  const int sub = threadIdx.x / kTpb;
+  const int lane = threadIdx.x % kTpb;
+  const long g = (long)blockIdx.x * kBlocksPerWg + sub;
+  if (g >= total_blocks) return;
+  const long bh = g / nblk;
+  const int I = (int)(g % nblk);
+  const int t0 = I * bs;
+  const int cnt = min(bs, N - t0);
+  const T *p = x + ((size_t)bh * N + t0) * D + lane * 8;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+#pragma unroll 8
+  for (int t = 0; t < cnt; ++t) {
+    if constexpr (sizeof(T) == 2) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(p + (size_t)t * D);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] = acc[2 * c] + __uint_as_float(ws[c] << 16);
+        acc[2 * c + 1] = acc[2 * c + 1] + __uint_as_float(ws[c] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4 *>(p + (size_t)t * D);
+      const float4 b = *reinterpret_cast<const float4 *>(p + (size_t)t * D + 4);
+      acc[0] = acc[0] + a.x; acc[1] = acc[1] + a.y; acc[2] = acc[2] + a.z; acc[3] = acc[3] + a.w;
+      acc[4] = acc[4] + b.x; acc[5] = acc[5] + b.y; acc[6] = acc[6] + b.z; acc[7] = acc[7] + b.w;
+    }
+  }
+  const float fc = (float)cnt;
+  float *o = out + (size_t)g * D + lane * 8;
+  float4 r0 = make_float4(acc[0] / fc, acc[1] / fc, acc[2] / fc, acc[3] / fc);
+  float4 r1 = make_float4(acc[4] / fc, acc[5] / fc, acc[6] / fc, acc[7] / fc);
+  *reinterpret_cast<float4 *>(o) = r0;
+  *reinterpret_cast<float4 *>(o + 4) = r1;
+}
+
+// ---------------------------------------------------------------- scores
+// S[bh, I, J] for a 64 x 64 tile per workgroup; each thread owns a 4 x 4 patch and keeps
+// one running sum per output, adding the rounded products in ascending d.
+constexpr int kSt = 64;    // tile edge
+constexpr int kSd = 32;    // d chunk staged in LDS
+constexpr int kSpad = 68;  // LDS row stride (floats)
+
+__global__ __launch_bounds__(256) void scores_kernel(const float *__restrict__ qbar,
+                                                     const float *__restrict__ kbar, int nQ,
+                                                     int nKV, int D, float c,
+                                                     float *__restrict__ S) {
+  __shared__ __align__(16) float qs[kSd][kSpad];
+  __shared__ __align__(16) float ks[kSd][kSpad];
+  const int bh = blockIdx.z;
+  const int i0 = blockIdx.y * kSt;
+  const int j0 = blockIdx.x * kSt;
+  const int tid = threadIdx.x;
+  const int ti = tid / 16, tj = tid % 16;
+  const float *qb = qbar + (size_t)bh * nQ * D;
+  const float *kb = kbar + (size_t)bh * nKV * D;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  for (int d0 = 0; d0 < D; d0 += kSd) {
+    for (int e = tid; e < kSt * kSd; e += 256) {
+      const int r = e / kSd, dd = e % kSd;
+      qs[dd][r] = (i0 + r < nQ) ? qb[(size_t)(i0 + r) * D + d0 + dd] : 0.0f;
+      ks[dd][r] = (j0 + r < nKV) ? kb[(size_t)(j0 + r) * D + d0 + dd] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int dd = 0; dd < kSd; ++dd) {
+      const float4 qa = *reinterpret_cast<const float4 *>(&qs[dd][ti * 4]);
+      const float4 kv = *reinterpret_cast<const float4 *>(&ks[dd][tj * 4]);
+      const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
+      const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float prod = qv[a] * kk[b];
+          acc[a][b] = acc[a][b] + prod;
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int I = i0 + ti * 4 + a;
+    if (I >= nQ) continue;
+    float *row = S + ((size_t)bh * nQ + I) * nKV;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int J = j0 + tj * 4 + b;
+      if (J < nKV) row[J] = acc[a][b] * c;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- selection
+__device__ __forceinline__ uint32_t desc_order_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 sorts with +0
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;  // ascending in this value = descending in f
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Adjacent-pair tree across the 64 lanes: after the step with stride s, every lane holds
+// the sum of its aligned group of 2s chunks, which is the next level of the tree.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float w = __shfl_xor(v, o);
+    v = v + w;
+  }
+  return v;
+}
+
+// One workgroup per row. Thread t owns blocks [t*ITEMS, (t+1)*ITEMS), so the in-thread
+// tree and the lane butterfly together form one adjacent-pair tree over 256*ITEMS
+// leaves; leaves past nKV are zero, which leaves the sum of a power-of-two prefix
+// unchanged.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S, int nKV,
+                                                     int m_k, float p, int p_all,
+                                                     uint32_t *__restrict__ bitmap,
+                                                     int nwords, int32_t *__restrict__ counts) {
+  constexpr int P = 256 * ITEMS;
+  __shared__ uint64_t keys[P];
+  __shared__ float ev[P];
+  __shared__ uint32_t bits[kMaxKvBlocks / 32];
+  __shared__ float red[4];
+  __shared__ int sh_count;
+
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const float *s = S + (size_t)row * nKV;
+
+  float sv[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int J = tid * ITEMS + i;
+    sv[i] = (J < nKV) ? s[J] : -INFINITY;
+  }
+  for (int w = tid; w < nwords; w += 256) bits[w] = 0u;
+
+  // row maximum (exact in any order)
+  float m = sv[0];
+#pragma unroll
+  for (int i = 1; i < ITEMS; ++i) m = fmaxf(m, sv[i]);
+  m = wave_max(m);
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+
+  // e_J, the keys, and the in-thread part of the tree
+  float tr[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int J = tid * ITEMS + i;
+    const bool ok = J < nKV;
+    const float e = ok ? exp_sa(sv[i] - m) : 0.0f;
+    tr[i] = e;
+    ev[tid * ITEMS + i] = e;
+    keys[tid * ITEMS + i] = ok ? (((uint64_t)desc_order_bits(sv[i]) << 32) | (uint32_t)J)
+                               : ~0ull;
+  }
+#pragma unroll
+  for (int w = ITEMS; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) tr[i] = tr[2 * i] + tr[2 * i + 1];
+  float z = wave_tree_sum(tr[0]);
+  if (lane == 0) red[wid] = z;
+  __syncthreads();
+  z = (red[0] + red[1]) + (red[2] + red[3]);
+  const float thr = p * z;
+
+  // bitonic sort of the keys, ascending
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P / 2; i += 256) {
+        const int lo = 2 * i - (i & (j - 1));
+        const int hi = lo + j;
+        const uint64_t a = keys[lo], b = keys[hi];
+        const bool up = (lo & k) == 0;
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // e in score order
+  float es[ITEMS];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int r = tid + q * 256;
+    es[q] = 0.0f;
+    if (r < nKV) es[q] = ev[(uint32_t)keys[r]];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) ev[tid + q * 256] = es[q];
+  __syncthreads();
+
+  // sequential top-p scan, one add at a time in score order. Wave 0 walks the sorted
+  // values 64 at a time: each value is broadcast from its lane and added to a running
+  // sum that every lane holds identically, lane u keeps the sum after position u, and a
+  // ballot finds the first position that reaches the threshold. All control flow here
+  // is wave-uniform.
+  if (wid == 0) {
+    int mp = nKV;
+    if (!p_all) {
+      float acc = 0.0f;
+      for (int c0 = 0; c0 < nKV; c0 += 64) {
+        const bool in = c0 + lane < nKV;
+        const float val = in ? ev[c0 + lane] : 0.0f;
+        const int vbits = __float_as_int(val);
+        float pre = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+          acc = acc + __int_as_float(__builtin_amdgcn_readlane(vbits, u));
+          pre = (lane == u) ? acc : pre;
+        }
+        const unsigned long long hit = __ballot(in && pre >= thr);
+        if (hit != 0ull) {
+          mp = c0 + __ffsll((long long)hit);
+          break;
+        }
+      }
+    }
+    if (lane == 0) sh_count = max(m_k, mp);
+  }
+  __syncthreads();
+  const int count = sh_count;
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int r = tid + q * 256;
+    if (r < count) {
+      const uint32_t J = (uint32_t)keys[r];
+      atomicOr(&bits[J >> 5], 1u << (J & 31));
+    }
+  }
+  __syncthreads();
+  for (int w = tid; w < nwords; w += 256) bitmap[(size_t)row * nwords + w] = bits[w];
+  if (tid == 0) counts[row] = count;
+}
+
+// ---------------------------------------------------------------- CSR
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ counts, int R,
+                                                    int32_t *__restrict__ row_ptr) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid == 0) {
+    carry = 0;
+    row_ptr[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < R; base += 1024) {
+    const int i = base + tid;
+    const int v = i < R ? counts[i] : 0;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+      int w = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const int y = __shfl_up(w, o);
+        if (lane >= o) w += y;
+      }
+      if (lane < 16) wsum[lane] = w;
+    }
+    __syncthreads();
+    const int incl = carry + (wid > 0 ? wsum[wid - 1] : 0) + x;
+    if (i < R) row_ptr[i + 1] = incl;
+    __syncthreads();
+    if (tid == 1023) carry = incl;
+    __syncthreads();
+  }
+}
+
+// One wave per row: popcounts, a lane prefix sum, then each lane writes its words' set
+// bits in ascending order.
+__global__ __launch_bounds__(256) void fill_kernel(const uint32_t *__restrict__ bitmap,
+                                                   int nwords, const int32_t *__restrict__ row_ptr,
+                                                   int R, int32_t *__restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  int running = row_ptr[row];
+  for (int w0 = 0; w0 < nwords; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t b = w < nwords ? bitmap[(size_t)row * nwords + w] : 0u;
+    const int c = __popc(b);
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    int pos = running + x - c;
+    while (b) {
+      const int bit = __ffs(b) - 1;
+      col_idx[pos++] = w * 32 + bit;
+      b &= b - 1;
+    }
+    running += __shfl(x, 63);
+  }
+}
+
+__global__ void dense_plan_kernel(int R, int nKV, int32_t *__restrict__ row_ptr,
+                                  int32_t *__restrict__ col_idx) {
+  const long total = (long)R * nKV;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    col_idx[i] = (int32_t)(i % nKV);
+    if (i % nKV == 0) row_ptr[i / nKV] = (int32_t)i;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[R] = (int32_t)total;
+}
+
+__global__ void identity_order_kernel(int R, int32_t *__restrict__ row_order) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < R) row_order[i] = i;
+}
+
+__global__ void router_exp_kernel(const float *__restrict__ x, float *__restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = exp_sa(x[i]);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int N, int D, int bs, float *out,
+                       hipStream_t s) {
+  const int nblk = ceil_div(N, bs);
+  const long total = (long)BH * nblk;
+  const int per_wg = 256 / (D / 8);
+  const unsigned grid = (unsigned)((total + per_wg - 1) / per_wg);
+  if (dt == SA_BF16) {
+    if (D == 128)
+      pool_kernel<uint16_t, 128><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);
+    else
+      pool_kernel<uint16_t, 64><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);
+  } else {
+    if (D == 128)
+      pool_kernel<float, 128><<<grid, 256, 0, s>>>((const float *)x, N, bs, nblk, total, out);
+    else
+      pool_kernel<float, 64><<<grid, 256, 0, s>>>((const float *)x, N, bs, nblk, total, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const float *qbar, const float *kbar, int BH, int nQ, int nKV, int D,
+                         float c, float *scores, hipStream_t s) {
+  dim3 grid(ceil_div(nKV, kSt), ceil_div(nQ, kSt), BH);
+  scores_kernel<<<grid, 256, 0, s>>>(qbar, kbar, nQ, nKV, D, c, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float *scores, int R, int nKV, int m_k, float p, int p_all,
+                         uint32_t *bitmap, int nwords, int32_t *counts, hipStream_t s) {
+  if (nKV <= 256)
+    select_kernel<1><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+  else if (nKV <= 512)
+    select_kernel<2><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+  else if (nKV <= 1024)
+    select_kernel<4><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+  else if (nKV <= 2048)
+    select_kernel<8><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+  else
+    select_kernel<16><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, hipStream_t s) {
+  scan_kernel<<<1, 1024, 0, s>>>(counts, R, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(const uint32_t *bitmap, int nwords, const int32_t *row_ptr, int R,
+                       int32_t *col_idx, hipStream_t s) {
+  fill_kernel<<<ceil_div(R, 4), 256, 0, s>>>(bitmap, nwords, row_ptr, R, col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+  const long total = (long)R * nKV;
+  long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  dense_plan_kernel<<<(unsigned)blocks, 256, 0, s>>>(R, nKV, row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_order(const int32_t *row_ptr, int R, int nKV, int32_t *row_order,
+                            int32_t *scratch, hipStream_t s) {
+  (void)row_ptr;
+  (void)nKV;
+  (void)scratch;
+  identity_order_kernel<<<ceil_div(R, 256), 256, 0, s>>>(R, row_order);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_exp(const float *x, float *y, int64_t n, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  router_exp_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, y, n);
+  return hipGetLastError();
+}
+
+}  // namespace sa

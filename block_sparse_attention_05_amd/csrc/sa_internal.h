@@ -1,0 +1,52 @@
+// Internal declarations shared by the library's translation units (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sparse_attn.h"
+
+namespace sa {
+
+constexpr int kMaxKvBlocks = 4096;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Router launchers (router.hip). All return hipSuccess or the launch error.
+hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int N, int D, int bs, float *out,
+                       hipStream_t s);
+hipError_t launch_scores(const float *qbar, const float *kbar, int BH, int nQ, int nKV, int D,
+                         float c, float *scores, hipStream_t s);
+hipError_t launch_select(const float *scores, int R, int nKV, int m_k, float p, int p_all,
+                         uint32_t *bitmap, int nwords, int32_t *counts, hipStream_t s);
+hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, hipStream_t s);
+hipError_t launch_fill(const uint32_t *bitmap, int nwords, const int32_t *row_ptr, int R,
+                       int32_t *col_idx, hipStream_t s);
+hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+hipError_t launch_row_order(const int32_t *row_ptr, int R, int nKV, int32_t *row_order,
+                            int32_t *scratch, hipStream_t s);
+hipError_t launch_router_exp(const float *x, float *y, int64_t n, hipStream_t s);
+
+// Attention launchers (attention.hip).
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *row_ptr, *col_idx, *row_order;
+  int B, H, N, D, block_q, block_kv, n_qblk, n_kvblk;
+  float scale_log2;        // log2(e) / sqrt(D)
+  double scale_log2_f64;   // the same in fp64
+  // linear branch (null alpha: off)
+  const float *alpha;      // [H, D]
+  const float *lin_h;      // [B*H, D, D] sum_j phi(k_j) v_j^T
+  const float *lin_z;      // [B*H, D]    sum_j phi(k_j)
+};
+hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s);
+hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int BH, int N, int D,
+                                 float *partial, int n_chunks, float *lin_h, float *lin_z,
+                                 hipStream_t s);
+int linear_prepass_chunks(int N);
+
+}  // namespace sa

@@ -1,0 +1,143 @@
+/*
+ * sparse_attn.h — block-sparse softmax attention for video DiTs on MI355X (gfx950).
+ *
+ * Two calls make the hot path:
+ *
+ *   sparse_attn_plan   the per-call block-mask router. Q and K are mean-pooled per block
+ *                      and per head (SLA2 page, router item 1; its learnable projection
+ *                      is the identity here), pooled blocks are scored, each query-block
+ *                      row gets a softmax over its KV-block scores, and the row keeps the
+ *                      union of its top-k% blocks and of the smallest set whose cumulative
+ *                      probability reaches p (SpargeAttention2 page, section 2(1), applied
+ *                      to blocks). The result is a CSR list of kept KV blocks per query
+ *                      block.
+ *   sparse_attn_fwd    FlashAttention-style attention that visits only the kept Q x KV
+ *                      tiles; masked tiles take no part in the products or the softmax
+ *                      (SpargeAttention2 page, section 2(3)). With alpha given, an elu+1
+ *                      linear-attention branch over each query block's masked-out KV
+ *                      blocks (SALAD page, section 2.1; SLA2 page: dropped blocks feed the
+ *                      linear branch) is blended as O = alpha*Os + (1-alpha)*Ol (SLA2 page,
+ *                      item 2).
+ *
+ * Conventions for every call:
+ *   - Q, K, V, O are contiguous [B, H, N, D] arrays in device memory, D innermost, in
+ *     the dtype passed (bf16 or fp32; O has the dtype of Q).
+ *   - Block I of a sequence covers tokens [I*bs, min(N, (I+1)*bs)); the last block may
+ *     be ragged. Row r = (b*H + h)*n_qblk + I; R = B*H*n_qblk rows.
+ *   - Attention is non-causal with logits q.k / sqrt(D).
+ *   - The library allocates no memory. The caller owns every buffer, including the
+ *     workspaces, whose sizes the *_workspace_bytes calls give; workspaces must be
+ *     256-byte aligned device memory.
+ *   - Every launch is asynchronous on the given stream; nothing synchronises. Calls on
+ *     different streams with different workspaces may run concurrently.
+ *   - Arguments are validated on the host before anything is launched; a call that
+ *     returns an error has launched nothing (except SA_ERR_HIP, which reports a failed
+ *     launch). Device faults surface at the caller's next synchronisation.
+ *   - Results are deterministic: the same inputs give bitwise-identical plans and
+ *     outputs (no floating-point atomics anywhere).
+ *   - Non-finite inputs give unspecified results.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, k or p outside [0, 1] */
+  SA_ERR_UNSUPPORTED = -2,   /* a valid but unsupported shape (D, block sizes, sizes) */
+  SA_ERR_WORKSPACE = -3,     /* workspace null, too small or misaligned */
+  SA_ERR_PLAN_MISMATCH = -4, /* plan made for other shapes or another dtype */
+  SA_ERR_BAD_CSR = -5,       /* malformed caller CSR (plan_from_csr) */
+  SA_ERR_HIP = -6            /* a HIP call or kernel launch failed */
+} sa_status;
+
+typedef enum { SA_BF16 = 0, SA_FP32 = 1 } sa_dtype;
+
+/* A block mask in CSR form. Plain data; row_ptr and col_idx point into the workspace
+ * the plan was built in and stay valid while that workspace lives. One plan may serve
+ * any number of sparse_attn_fwd calls. */
+typedef struct sa_plan {
+  int32_t B, H, N, D;
+  int32_t block_q, block_kv;
+  int32_t n_qblk, n_kvblk;   /* ceil(N/block_q), ceil(N/block_kv) */
+  int32_t dtype;             /* sa_dtype of the Q and K the plan was built for */
+  int32_t reserved;
+  int32_t *row_ptr;          /* device, [R + 1], row_ptr[0] = 0, row_ptr[R] = nnz */
+  int32_t *col_idx;          /* device, capacity R * n_kvblk; ascending within a row */
+  int32_t *row_order;        /* device, [R]: rows by descending kept count (work order) */
+} sa_plan;
+
+/* Accepted shapes: D in {64, 128}; block_q in {64, 128}; block_kv = 64; B*H <= 65535;
+ * n_kvblk <= 4096; B*H*n_qblk*n_kvblk < 2^31. */
+
+/* Workspace bytes that sparse_attn_plan / _plan_dense / _plan_from_csr need; 0 when the
+ * shape is invalid or unsupported. */
+size_t sparse_attn_plan_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv);
+
+/* The hybrid top-k / top-p router (SpargeAttention2 page, section 2(1); SLA2 page,
+ * router item 1). q, k: device [B, H, N, D] in dtype. topk_frac: the top-k rule keeps
+ * m_k = min(nKV, max(1, ceil(topk_frac*nKV - 1e-9))) blocks per row; top_p: the top-p
+ * rule keeps the shortest score-ordered prefix whose cumulative softmax mass reaches
+ * top_p (all blocks when top_p >= 1). Each row keeps the union, which is the longer of
+ * the two prefixes of one order (scores descending, ties to the lower block index).
+ * Pooling, scores, softmax and the cumulative sums follow one fixed fp32 order, so the
+ * mask is exactly reproducible. On success *out describes the plan. */
+sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype,
+                           int B, int H, int N, int D, int block_q, int block_kv,
+                           double topk_frac, double top_p,
+                           void *workspace, size_t ws_bytes, sa_plan *out, hipStream_t stream);
+
+/* The all-ones mask (every query block keeps every KV block): dense attention through the
+ * same forward kernel. */
+sa_status sparse_attn_plan_dense(sa_dtype dtype, int B, int H, int N, int D, int block_q,
+                                 int block_kv, void *workspace, size_t ws_bytes,
+                                 sa_plan *out, hipStream_t stream);
+
+/* A caller-given mask. host_row_ptr [R + 1] and host_col_idx [host_row_ptr[R]] are HOST
+ * arrays, checked before use (row_ptr starts at 0 and never decreases; columns in
+ * [0, n_kvblk) and strictly ascending within a row) and copied into the workspace;
+ * the call returns once the host arrays may be reused. Rows may be empty: such a row's
+ * outputs are 0 (and its LSE -inf). */
+sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, int block_q,
+                                    int block_kv, const int32_t *host_row_ptr,
+                                    const int32_t *host_col_idx, void *workspace,
+                                    size_t ws_bytes, sa_plan *out, hipStream_t stream);
+
+/* Workspace bytes sparse_attn_fwd needs: 0 without the linear branch. */
+size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_linear);
+
+/* Block-sparse attention over the plan's kept tiles (SpargeAttention2 page, section 2(3)).
+ * q, k, v: device [B, H, N, D] in dtype; the shapes and dtype must equal the plan's.
+ * alpha: device float [H, D] or NULL. With alpha, the linear branch (SALAD page, section
+ * 2.1) covers each query block's masked-out KV blocks with phi = elu + 1 on the raw q
+ * and k, Ol = phi(q).sum_j phi(k_j) v_j^T / phi(q).sum_j phi(k_j) (0 when a query block
+ * keeps every KV block), and o = alpha*Os + (1-alpha)*Ol (SLA2 page, item 2).
+ * o: device [B, H, N, D] in dtype. lse: device float [B, H, N] or NULL; receives the
+ * natural-log sum of exp(logits) over kept tokens (-inf for an empty row).
+ * workspace: sparse_attn_fwd_workspace_bytes bytes (may be NULL when that is 0). */
+sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype dtype,
+                          int B, int H, int N, int D, const sa_plan *plan,
+                          const float *alpha, void *o, float *lse,
+                          void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Diagnostic: y[i] = the router's fp32 exp of x[i] for x[i] <= 0 (0 below -86), evaluated
+ * on the device with the router's own code. x, y: device float [n]. */
+sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream);
+
+/* A static description of a status code. */
+const char *sparse_attn_status_string(sa_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sparse_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,142 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every declared
+symbol, sizes workspaces, and rejects every invalid argument on the host before any HIP
+call (so these checks make no device call)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_05_amd as sa
+from block_sparse_attention_05_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000      # 256-aligned non-null "device" address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sa.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sparse_attn.h")).read()
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert len(decl) == 9
+    assert sorted(B.EXPORTS) == decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for st in range(-6, 1):
+        s = lib.sparse_attn_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.sparse_attn_status_string(-99).decode() == "unknown status"
+    assert sa.version() >= 100
+
+
+def test_workspace_sizes(lib):
+    f = lib.sparse_attn_plan_workspace_bytes
+    assert f(1, 40, 75600, 128, 128, 64) > 0
+    assert f(1, 8, 245760, 128, 128, 64) > 0
+    assert f(1, 2, 1024, 64, 64, 64) > 0
+    assert f(1, 1, 1024, 96, 64, 64) == 0         # unsupported D
+    assert f(1, 1, 1024, 64, 32, 64) == 0         # unsupported block_q
+    assert f(1, 1, 1024, 64, 64, 128) == 0        # unsupported block_kv
+    assert f(0, 1, 1024, 64, 64, 64) == 0
+    assert f(1, 1, 64 * 4097, 64, 64, 64) == 0    # too many KV blocks per row
+    # the workspace holds at least the CSR at full capacity
+    R, nkv = 40 * 591, 1182
+    assert f(1, 40, 75600, 128, 128, 64) >= 4 * (R + 1 + R * nkv)
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 12, 32760, 128, 0) == 0
+
+
+def plan_call(lib, q=FAKE, k=FAKE, dt=0, shape=(1, 2, 1024, 64, 64, 64), topk=0.25, p=0.9,
+              ws=FAKE, wsb=1 << 40, out=True):
+    st = B.SaPlan()
+    return lib.sparse_attn_plan(q, k, dt, *shape, topk, p, ws, wsb,
+                                ctypes.byref(st) if out else None, None)
+
+
+def test_plan_validation(lib):
+    E = B
+    assert plan_call(lib, q=None) == E.SA_ERR_INVALID_ARG
+    assert plan_call(lib, k=None) == E.SA_ERR_INVALID_ARG
+    assert plan_call(lib, out=False) == E.SA_ERR_INVALID_ARG
+    assert plan_call(lib, dt=7) == E.SA_ERR_INVALID_ARG
+    for bad in (-0.01, 1.01, math.nan, math.inf):
+        assert plan_call(lib, topk=bad) == E.SA_ERR_INVALID_ARG
+        assert plan_call(lib, p=bad) == E.SA_ERR_INVALID_ARG
+    assert plan_call(lib, shape=(1, 2, 0, 64, 64, 64)) == E.SA_ERR_INVALID_ARG
+    assert plan_call(lib, shape=(1, -2, 1024, 64, 64, 64)) == E.SA_ERR_INVALID_ARG
+    assert plan_call(lib, shape=(1, 2, 1024, 80, 64, 64)) == E.SA_ERR_UNSUPPORTED
+    assert plan_call(lib, shape=(1, 2, 1024, 64, 256, 64)) == E.SA_ERR_UNSUPPORTED
+    assert plan_call(lib, shape=(1, 2, 1024, 64, 64, 32)) == E.SA_ERR_UNSUPPORTED
+    assert plan_call(lib, ws=None) == E.SA_ERR_WORKSPACE
+    assert plan_call(lib, wsb=1000) == E.SA_ERR_WORKSPACE
+    assert plan_call(lib, ws=FAKE + 64) == E.SA_ERR_WORKSPACE
+
+
+def csr_call(lib, rp, ci, shape=(1, 1, 256, 64, 64, 64)):
+    st = B.SaPlan()
+    rp = np.ascontiguousarray(rp, np.int32)
+    ci = np.ascontiguousarray(ci, np.int32)
+    return lib.sparse_attn_plan_from_csr(0, *shape, rp.ctypes.data, ci.ctypes.data if ci.size else None,
+                                         FAKE, 1 << 40, ctypes.byref(st), None)
+
+
+def test_plan_from_csr_validation(lib):
+    # 256 tokens, 64-blocks: 4 rows, 4 KV blocks each
+    assert csr_call(lib, [1, 1, 2, 3, 4], [0, 1, 2, 3]) == B.SA_ERR_BAD_CSR         # row_ptr[0] != 0
+    assert csr_call(lib, [0, 2, 1, 3, 4], [0, 1, 2, 3]) == B.SA_ERR_BAD_CSR         # decreasing
+    assert csr_call(lib, [0, 1, 2, 3, 4], [0, 1, 4, 3]) == B.SA_ERR_BAD_CSR         # out of range
+    assert csr_call(lib, [0, 1, 2, 3, 4], [0, -1, 2, 3]) == B.SA_ERR_BAD_CSR        # negative
+    assert csr_call(lib, [0, 2, 2, 2, 2], [1, 0]) == B.SA_ERR_BAD_CSR               # unsorted
+    assert csr_call(lib, [0, 2, 2, 2, 2], [1, 1]) == B.SA_ERR_BAD_CSR               # duplicate
+    assert csr_call(lib, [0, 5, 5, 5, 5], [0, 1, 2, 3, 3]) == B.SA_ERR_BAD_CSR      # too many
+    assert csr_call(lib, [0, 1, 1, 1, 1], []) == B.SA_ERR_INVALID_ARG               # cols missing
+
+
+def fwd_call(lib, plan_fields, shape=(1, 2, 1024, 64), dt=0, alpha=None, ws=None, wsb=0,
+             q=FAKE, o=FAKE):
+    st = B.SaPlan(*plan_fields)
+    return lib.sparse_attn_fwd(q, FAKE, FAKE, dt, *shape, ctypes.byref(st), alpha, o, None, ws, wsb,
+                               None)
+
+
+def test_fwd_validation(lib):
+    good = (1, 2, 1024, 64, 64, 64, 16, 16, 0, 0, FAKE, FAKE, FAKE)
+    assert fwd_call(lib, good, q=None) == B.SA_ERR_INVALID_ARG
+    assert fwd_call(lib, good, o=None) == B.SA_ERR_INVALID_ARG
+    assert fwd_call(lib, good, shape=(1, 2, 1000, 64)) == B.SA_ERR_PLAN_MISMATCH
+    assert fwd_call(lib, good, shape=(1, 3, 1024, 64)) == B.SA_ERR_PLAN_MISMATCH
+    assert fwd_call(lib, good, dt=1) == B.SA_ERR_PLAN_MISMATCH
+    bad_blocks = (1, 2, 1024, 64, 64, 32, 16, 32, 0, 0, FAKE, FAKE, FAKE)
+    assert fwd_call(lib, bad_blocks) == B.SA_ERR_UNSUPPORTED
+    no_rows = (1, 2, 1024, 64, 64, 64, 16, 16, 0, 0, None, None, None)
+    assert fwd_call(lib, no_rows) == B.SA_ERR_INVALID_ARG
+    # the linear branch needs its workspace
+    need = lib.sparse_attn_fwd_workspace_bytes(1, 2, 1024, 64, 1)
+    if need > 0:
+        assert fwd_call(lib, good, alpha=FAKE) == B.SA_ERR_WORKSPACE
+        assert fwd_call(lib, good, alpha=FAKE, ws=FAKE, wsb=need - 1) == B.SA_ERR_WORKSPACE
+
+
+def test_router_exp_validation(lib):
+    assert lib.sparse_attn_router_exp(None, None, -1, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_exp(None, FAKE, 10, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_router_exp(None, None, 0, None) == B.SA_OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        sa.plan(q, q, 64, 64)
