@@ -27,6 +27,7 @@ COMMON = [
 SOURCES = {
     "router.hip": ["-ffp-contract=off"],
     "attention.hip": [],
+    "linear.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

@@ -84,15 +84,15 @@ void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
 
-// Linear-branch workspace: per head sum_j phi(k_j) v_j^T [D, D], sum_j phi(k_j) [D], and
-// per-chunk partials of both.
+// Linear-branch workspace: per head H^T (bf16 [D, D]) and z (fp32 [D]), the per-chunk
+// partials of both (fp32), and the fp32 linear output Ol [B, H, N, D].
 struct FwdLayout {
-  size_t lin_h, lin_z, partial, total;
+  size_t lin_ht, lin_z, partial, ol, total;
   int chunks;
 };
 
 FwdLayout fwd_layout(const Shape &s, int with_linear) {
-  FwdLayout L{0, 0, 0, 0, 0};
+  FwdLayout L{0, 0, 0, 0, 0, 0};
   if (!with_linear) return L;
   const size_t BH = (size_t)s.B * s.H;
   L.chunks = linear_prepass_chunks(s.N);
@@ -102,9 +102,10 @@ FwdLayout fwd_layout(const Shape &s, int with_linear) {
     off = align_up(off + bytes);
     return at;
   };
-  L.lin_h = take(BH * s.D * s.D * 4);
+  L.lin_ht = take(BH * s.D * s.D * 2);
   L.lin_z = take(BH * s.D * 4);
   L.partial = take(BH * (size_t)L.chunks * s.D * (s.D + 1) * 4);
+  L.ol = take(BH * (size_t)s.N * s.D * 4);
   L.total = off;
   return L;
 }
@@ -254,7 +255,7 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   const FwdLayout L = fwd_layout(s, alpha != nullptr);
   st = check_ws(workspace, ws_bytes, L.total);
   if (st != SA_OK) return st;
-  if (alpha != nullptr) return SA_ERR_UNSUPPORTED;  // linear branch not built yet
+  if (alpha != nullptr && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;  // linear branch: bf16
 
   FwdArgs a{};
   a.q = q;
@@ -276,8 +277,20 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   a.scale_log2_f64 = 1.4426950408889634 / sqrt((double)D);
   a.alpha = nullptr;
-  a.lin_h = nullptr;
-  a.lin_z = nullptr;
+  a.ol = nullptr;
+  if (alpha != nullptr) {
+    char *ws = static_cast<char *>(workspace);
+    uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.lin_ht);
+    float *z = reinterpret_cast<float *>(ws + L.lin_z);
+    float *ol = reinterpret_cast<float *>(ws + L.ol);
+    hipError_t e = launch_linear_prepass(k, v, dtype, B * H, N, D,
+                                         reinterpret_cast<float *>(ws + L.partial), L.chunks, ht,
+                                         z, stream);
+    if (e == hipSuccess) e = launch_linear_apply(a, ht, z, ol, stream);
+    if (e != hipSuccess) return SA_ERR_HIP;
+    a.alpha = alpha;
+    a.ol = ol;
+  }
   return hip_status(launch_fwd(a, dtype, stream));
 }
 

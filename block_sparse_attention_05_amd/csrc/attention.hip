@@ -88,7 +88,7 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return (b % 8) * q + b / 8;
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool LIN>
 __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
   using E = Elem<T>;
   constexpr int NT = 64 * NW;             // threads
@@ -132,10 +132,19 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
   const int end = a.row_ptr[row + 1];
 
   if (beg == end) {
-    // no kept tile: zero output, -inf LSE
+    // no kept tile: Os = 0 (so O = (1 - alpha) * Ol with the linear branch), -inf LSE
     if (q_ok) {
-      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4)
-        store4<T>(og + (size_t)qi * D + d, 0.f, 0.f, 0.f, 0.f);
+      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4) {
+        if constexpr (LIN) {
+          const int h = bh % a.H;
+          const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)h * D + d);
+          const float4 lv = *reinterpret_cast<const float4 *>(a.ol + head + (size_t)qi * D + d);
+          store4<T>(og + (size_t)qi * D + d, (1.f - al.x) * lv.x, (1.f - al.y) * lv.y,
+                    (1.f - al.z) * lv.z, (1.f - al.w) * lv.w);
+        } else {
+          store4<T>(og + (size_t)qi * D + d, 0.f, 0.f, 0.f, 0.f);
+        }
+      }
       if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = -INFINITY;
     }
     return;
@@ -394,8 +403,19 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = t * 32 + g * 8 + hf * 4;
-        store4<T>(orow + d, oacc[t][g * 4 + 0] * inv, oacc[t][g * 4 + 1] * inv,
-                  oacc[t][g * 4 + 2] * inv, oacc[t][g * 4 + 3] * inv);
+        float o0 = oacc[t][g * 4 + 0] * inv, o1 = oacc[t][g * 4 + 1] * inv;
+        float o2 = oacc[t][g * 4 + 2] * inv, o3 = oacc[t][g * 4 + 3] * inv;
+        if constexpr (LIN) {
+          // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel)
+          const int h = bh % a.H;
+          const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)h * D + d);
+          const float4 lv = *reinterpret_cast<const float4 *>(a.ol + head + (size_t)qi * D + d);
+          o0 = al.x * o0 + (1.f - al.x) * lv.x;
+          o1 = al.y * o1 + (1.f - al.y) * lv.y;
+          o2 = al.z * o2 + (1.f - al.z) * lv.z;
+          o3 = al.w * o3 + (1.f - al.w) * lv.w;
+        }
+        store4<T>(orow + d, o0, o1, o2, o3);
       }
     if (a.lse && hf == 0) {
       if constexpr (sizeof(T) == 2)
@@ -406,28 +426,26 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool LIN>
 hipError_t launch_t(const FwdArgs &a, hipStream_t s) {
   const int R = a.B * a.H * a.n_qblk;
   if (a.block_q == 128)
-    sparse_fwd_kernel<T, D, 4><<<R, 256, 0, s>>>(a);
+    sparse_fwd_kernel<T, D, 4, LIN><<<R, 256, 0, s>>>(a);
   else
-    sparse_fwd_kernel<T, D, 2><<<R, 128, 0, s>>>(a);
+    sparse_fwd_kernel<T, D, 2, LIN><<<R, 128, 0, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s) {
-  if (dt == SA_BF16) return a.D == 128 ? launch_t<uint16_t, 128>(a, s) : launch_t<uint16_t, 64>(a, s);
-  return a.D == 128 ? launch_t<float, 128>(a, s) : launch_t<float, 64>(a, s);
-}
-
-int linear_prepass_chunks(int N) { (void)N; return 0; }
-
-hipError_t launch_linear_prepass(const void *, const void *, sa_dtype, int, int, int, float *, int,
-                                 float *, float *, hipStream_t) {
-  return hipErrorNotSupported;
+  if (a.alpha != nullptr) {
+    if (dt != SA_BF16) return hipErrorNotSupported;
+    return a.D == 128 ? launch_t<uint16_t, 128, true>(a, s) : launch_t<uint16_t, 64, true>(a, s);
+  }
+  if (dt == SA_BF16)
+    return a.D == 128 ? launch_t<uint16_t, 128, false>(a, s) : launch_t<uint16_t, 64, false>(a, s);
+  return a.D == 128 ? launch_t<float, 128, false>(a, s) : launch_t<float, 64, false>(a, s);
 }
 
 }  // namespace sa

@@ -40,13 +40,16 @@ struct FwdArgs {
   double scale_log2_f64;   // the same in fp64
   // linear branch (null alpha: off)
   const float *alpha;      // [H, D]
-  const float *lin_h;      // [B*H, D, D] sum_j phi(k_j) v_j^T
-  const float *lin_z;      // [B*H, D]    sum_j phi(k_j)
+  const float *ol;         // [B, H, N, D] fp32 linear-branch output Ol
 };
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s);
+// Linear branch (linear.hip): per-head H^T = sum_j v_j phi(k_j)^T (bf16 [B*H, D, D]) and
+// z = sum_j phi(k_j) (fp32 [B*H, D]); then Ol per query block over its masked-out blocks.
 hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int BH, int N, int D,
-                                 float *partial, int n_chunks, float *lin_h, float *lin_z,
+                                 float *partial, int n_chunks, uint16_t *lin_ht, float *lin_z,
                                  hipStream_t s);
+hipError_t launch_linear_apply(const FwdArgs &a, const uint16_t *lin_ht, const float *lin_z,
+                               float *ol, hipStream_t s);
 int linear_prepass_chunks(int N);
 
 }  // namespace sa
