@@ -27,6 +27,7 @@ COMMON = [
 SOURCES = {
     "router.hip": ["-ffp-contract=off"],
     "attention.hip": [],
+    "sparse_fwd_bf16.hip": [],
     "linear.hip": [],
     "api.cpp": ["-x", "hip"],
 }

@@ -14,7 +14,8 @@
 // K tiles are staged row-major in LDS; V tiles are transposed on the way into LDS so the
 // V^T operand is a pair of 8-byte reads. The next tile's global loads are issued before
 // the current tile's math.
-// Element types: bf16 (bf16 MFMA, fp32 accumulation) or fp32 (fp32 MFMA).
+// This file instantiates the kernel for fp32 inputs (fp64 scores, fp32 MFMA for P V);
+// bf16 inputs use the tuned kernel in sparse_fwd_bf16.hip.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -439,12 +440,8 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s) {
-  if (a.alpha != nullptr) {
-    if (dt != SA_BF16) return hipErrorNotSupported;
-    return a.D == 128 ? launch_t<uint16_t, 128, true>(a, s) : launch_t<uint16_t, 64, true>(a, s);
-  }
-  if (dt == SA_BF16)
-    return a.D == 128 ? launch_t<uint16_t, 128, false>(a, s) : launch_t<uint16_t, 64, false>(a, s);
+  if (dt == SA_BF16) return launch_fwd_bf16(a, s);
+  if (a.alpha != nullptr) return hipErrorNotSupported;
   return a.D == 128 ? launch_t<float, 128, false>(a, s) : launch_t<float, 64, false>(a, s);
 }
 

@@ -43,6 +43,7 @@ struct FwdArgs {
   const float *ol;         // [B, H, N, D] fp32 linear-branch output Ol
 };
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);  // sparse_fwd_bf16.hip
 // Linear branch (linear.hip): per-head H^T = sum_j v_j phi(k_j)^T (bf16 [B*H, D, D]) and
 // z = sum_j phi(k_j) (fp32 [B*H, D]); then Ol per query block over its masked-out blocks.
 hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int BH, int N, int D,
