@@ -13,10 +13,13 @@
 //                    probability to bf16 then shows up at full weight in outputs that
 //                    one key dominates;
 //   O^T += V^T P^T   bf16 MFMA; P packed with v_cvt_pk_bf16_f32.
-// K tiles are staged row-major in LDS, V tiles transposed on the way in; the next tile's
-// global loads are in flight during the current tile's math. The ragged last KV block (if
-// kept) is always the last tile of a row, because kept lists are ascending, so only that
-// tile carries the key mask.
+// K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4), row-major with
+// one pad granule per row, double-buffered: the next tile's loads are in flight while the
+// current tile is computed, with one barrier per tile. The V^T operand is read with the
+// transposing LDS read ds_read_b64_tr_b16, so V needs no transposition on the way in. The
+// ragged last KV block (if kept) is always the last tile of a row, because kept lists
+// are ascending; its rows past N reload the last valid row, and only that tile carries
+// the key mask.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,7 +32,15 @@ namespace sa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+typedef __attribute__((address_space(3))) bf16x4_t lbf16x4_t;
+
+// s_waitcnt immediate that waits for all vector-memory operations (direct LDS loads
+// included) and leaves the export and LDS counters unconstrained
+constexpr int kVmcnt0 = 0x0F70;
 
 constexpr int kBk = 64;            // keys per tile
 
@@ -54,17 +65,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
-  constexpr int KROW = D + 8;               // K tile row stride (elements)
-  constexpr int VROW = kBk + 4;             // V^T tile row stride (elements)
-  constexpr int KCH = kBk * D / 8;          // 16-byte chunks per K tile
-  constexpr int KPT = (KCH + NT - 1) / NT;
-  constexpr int VCH = (kBk / 4) * (D / 8);  // 4-row x 8-column chunks per V tile
-  constexpr int VPT = (VCH + NT - 1) / NT;
+  constexpr int GR = D / 8 + 1;             // 16-byte granules per LDS row (one pad granule)
+  constexpr int ROWB = GR * 16;             // bytes per LDS row
+  constexpr int NI = GR;                    // 1 KB direct loads per 64-row tile (64*GR/64)
+  constexpr int NIW = (NI + NW - 1) / NW;   // direct loads per wave and matrix
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
 
-  __shared__ __align__(16) uint16_t ks[kBk * KROW];
-  __shared__ __align__(16) uint16_t vt[D * VROW];
+  // double-buffered K and V tiles, row-major [key][channel] with padded rows; separate
+  // arrays so the compiler can tell the in-flight loads from the tile being read
+  __shared__ __align__(16) char k0s[kBk * ROWB];
+  __shared__ __align__(16) char v0s[kBk * ROWB];
+  __shared__ __align__(16) char k1s[kBk * ROWB];
+  __shared__ __align__(16) char v1s[kBk * ROWB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,63 +132,45 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
   }
 
-  uint4 kr[KPT];
-  uint4 vr[VPT][4];
+  // Direct HBM -> LDS tile loads. Load i of a matrix fills LDS granules 64i .. 64i+63 of
+  // the padded tile; lane p of it carries granule 64i + p = (row r, column granule c).
+  // Pad granules (c == D/8) reload granule 0 of their row. Wave w issues loads w, w+NW, ...
+  int goff[NIW];      // byte offset of the lane's source granule within a 64-row tile
+#pragma unroll
+  for (int m = 0; m < NIW; ++m) {
+    const int p = 64 * (wid + m * NW) + lane;
+    const int c = p % GR;
+    goff[m] = ((p / GR) * D + (c < D / 8 ? c : 0) * 8) * 2;
+  }
+  const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
+  const int32_t *__restrict__ cols = a.col_idx + beg;
 
-  auto load_tile = [&](int J) {
+  auto issue = [&](int J, char *kdst, char *vdst) {
     const int j0 = J * kBk;
+    const char *kb = reinterpret_cast<const char *>(kg + (size_t)j0 * D);
+    const char *vb = reinterpret_cast<const char *>(vg + (size_t)j0 * D);
+    if (J != ragged_blk) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * NT;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      if (c < KCH) {
-        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-        if (j0 + r < N) kr[u] = *reinterpret_cast<const uint4 *>(kg + (size_t)(j0 + r) * D + col);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * NT;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vr[u][rr] = make_uint4(0, 0, 0, 0);
-      if (c < VCH) {
-        const int kgp = c / (D / 8), col = (c % (D / 8)) * 8;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = j0 + kgp * 4 + rr;
-          if (r < N) vr[u][rr] = *reinterpret_cast<const uint4 *>(vg + (size_t)r * D + col);
+      for (int m = 0; m < NIW; ++m) {
+        const int i = wid + m * NW;
+        if (i < NI) {
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + goff[m]), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
         }
       }
-    }
-  };
-
-  auto store_tile = [&]() {
+    } else {
+      // the ragged last block: rows past N reload the last valid row (in bounds, finite)
+      const int last = N - 1 - j0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * NT;
-      if (c < KCH) {
-        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<uint4 *>(&ks[r * KROW + col]) = kr[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * NT;
-      if (c < VCH) {
-        const int kgp = c / (D / 8), col = (c % (D / 8)) * 8;
-        const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&vr[u][0]);
-        const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vr[u][1]);
-        const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vr[u][2]);
-        const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&vr[u][3]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          uint2 lo, hi;
-          lo.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u);
-          hi.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
-          hi.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u);
-          *reinterpret_cast<uint2 *>(&vt[(col + 2 * m) * VROW + kgp * 4]) = lo;
-          *reinterpret_cast<uint2 *>(&vt[(col + 2 * m + 1) * VROW + kgp * 4]) = hi;
+      for (int m = 0; m < NIW; ++m) {
+        const int i = wid + m * NW;
+        if (i < NI) {
+          const int p = 64 * i + lane;
+          const int c = p % GR;
+          const int r = min(p / GR, last);
+          const int off = (r * D + (c < D / 8 ? c : 0) * 8) * 2;
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + off), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + off), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
         }
       }
     }
@@ -189,18 +184,26 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running max, scaled logits, log2 domain
   float l_run = 0.0f;       // this lane's part of the running sum
   const float sl2 = a.scale_log2;
-  const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
 
-  auto tile = [&](int J, auto mask_tag) {
+  // per-lane LDS byte offsets: K operand row l32, granule hf; V^T operand source row
+  // (hf*4 + u/4), channel 16*(group & 1) + 4*(u & 3), u = lane & 15
+  const int koff = l32 * ROWB + hf * 16;
+  const int u = lane & 15;
+  const int voff = (hf * 4 + (u >> 2)) * ROWB + (16 * ((lane >> 4) & 1) + 4 * (u & 3)) * 2;
+
+  auto tile = [&](int J, const char *kt_s, const char *vt_s, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     floatx16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.0f;
+    // the two 32-key blocks interleave, so consecutive MFMAs do not share an accumulator
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(&ks[(kt * 32 + l32) * KROW + s * 16 + hf * 8]);
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(kt_s + koff + kt * 32 * ROWB + s * 32);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[s],
                                                            sacc[kt], 0, 0, 0);
       }
@@ -243,8 +246,9 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
         psum += pv;
       }
     l_run += psum;
-    // O^T += V^T P^T; reduction index hf*8 + e stands for key base + (e/4)*8 + hf*4 + e%4,
-    // which is where the S^T layout left this lane's probabilities.
+    // O^T += V^T P^T. Reduction index hf*8 + e stands for key base + (e/4)*8 + hf*4 + e%4,
+    // where the S^T layout left this lane's probabilities; the V^T operand comes from two
+    // transposing LDS reads of keys base + hf*4 + 0..3 and base + 8 + hf*4 + 0..3.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kt = s / 2, i0 = (s % 2) * 8;
@@ -254,35 +258,44 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kt][i0 + e];
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const uint16_t *vrow = &vt[(t * 32 + l32) * VROW + base + hf * 4];
-        const uint2 v0 = *reinterpret_cast<const uint2 *>(vrow);
-        const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 8);
-        const uint4 vw = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pb,
-                                                          oacc[t], 0, 0, 0);
+        const char *p0 = vt_s + voff + base * ROWB + t * 64;
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(p0));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(p0 + 8 * ROWB));
+        const bf16x8_t vw = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw, pb, oacc[t], 0, 0, 0);
       }
     }
   };
 
-  // all tiles but the last: never the ragged block
-  load_tile(a.col_idx[beg]);
-  for (int it = beg; it < end - 1; ++it) {
-    const int J = a.col_idx[it];
+  // Two tiles per trip so the buffer of each tile is fixed at compile time. Only full
+  // tiles run in the loop; the ragged block, when kept, is the row's last tile and runs
+  // after it with the key mask.
+  const int n = end - beg;
+  const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
+  issue(cols[0], k0s, v0s);
+  int it = 0;
+  for (; it < n_full; it += 2) {
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    store_tile();
+    if (it + 1 < n) issue(cols[it + 1], k1s, v1s);
+    tile(cols[it], k0s, v0s, std::false_type{});
+    if (it + 1 >= n_full) {
+      ++it;
+      break;
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    load_tile(a.col_idx[it + 1]);
-    tile(J, std::false_type{});
+    if (it + 2 < n) issue(cols[it + 2], k0s, v0s);
+    tile(cols[it + 1], k1s, v1s, std::false_type{});
   }
-  {
-    const int J = a.col_idx[end - 1];
+  if (n_full < n) {
+    // tile n - 1 was issued into buffer (n - 1) % 2
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (J == ragged_blk)
-      tile(J, std::true_type{});
+    if ((n - 1) % 2 == 0)
+      tile(cols[n - 1], k0s, v0s, std::true_type{});
     else
-      tile(J, std::false_type{});
+      tile(cols[n - 1], k1s, v1s, std::true_type{});
   }
 
   // epilogue: normalise (and blend), store bf16
