@@ -197,10 +197,23 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
   return v;
 }
 
+constexpr int kCandCap = 512;   // largest candidate set ranked without the full sort
+
 // One workgroup per row. Thread t owns blocks [t*ITEMS, (t+1)*ITEMS), so the in-thread
 // tree and the lane butterfly together form one adjacent-pair tree over 256*ITEMS
 // leaves; leaves past nKV are zero, which leaves the sum of a power-of-two prefix
 // unchanged.
+//
+// Only the first max(m_k, m_p) blocks of the score order matter, so the row is not
+// sorted in full when a small candidate set provably contains them: with e_J binned by
+// exponent, the bins from the top down to bin b hold the blocks with e >= 2^(b-127),
+// which is a top set of the score order (exp_sa is monotone, so equal scores share a
+// bin). Each bin also sums its e_J in 2^-40 fixed point (integer adds: exact and
+// order-free; truncation keeps it a lower bound). The first such set with at least m_k
+// blocks whose mass bound exceeds thr by 2^-10 (more than the relative error of any fp32
+// running sum over at most kCandCap terms) contains the top-p crossing. Its blocks are
+// ranked by counting, then scanned exactly as the full sort would be. Rows whose set is
+// larger than kCandCap take the full bitonic sort.
 template <int ITEMS>
 __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S, int nKV,
                                                      int m_k, float p, int p_all,
@@ -210,8 +223,13 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
   __shared__ uint64_t keys[P];
   __shared__ float ev[P];
   __shared__ uint32_t bits[kMaxKvBlocks / 32];
+  __shared__ uint64_t cand[kCandCap];
+  __shared__ uint64_t csort[kCandCap];
+  __shared__ float cev[kCandCap];
+  __shared__ int hist[128];
+  __shared__ unsigned long long hmass[128];   // per-bin sum of e in 2^-40 fixed point
   __shared__ float red[4];
-  __shared__ int sh_count;
+  __shared__ int sh_count, sh_ncand, sh_bstar, sh_pos;
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -225,6 +243,10 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
     sv[i] = (J < nKV) ? s[J] : -INFINITY;
   }
   for (int w = tid; w < nwords; w += 256) bits[w] = 0u;
+  if (tid < 128) {
+    hist[tid] = 0;
+    hmass[tid] = 0ull;
+  }
 
   // row maximum (exact in any order)
   float m = sv[0];
@@ -238,6 +260,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
 
   // e_J, the keys, and the in-thread part of the tree
   float tr[ITEMS];
+  uint64_t kv[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int J = tid * ITEMS + i;
@@ -245,8 +268,12 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
     const float e = ok ? exp_sa(sv[i] - m) : 0.0f;
     tr[i] = e;
     ev[tid * ITEMS + i] = e;
-    keys[tid * ITEMS + i] = ok ? (((uint64_t)desc_order_bits(sv[i]) << 32) | (uint32_t)J)
-                               : ~0ull;
+    kv[i] = ok ? (((uint64_t)desc_order_bits(sv[i]) << 32) | (uint32_t)J) : ~0ull;
+    if (ok) {
+      const int b = __float_as_uint(e) >> 23;
+      atomicAdd(&hist[b], 1);
+      atomicAdd(&hmass[b], (unsigned long long)(e * 0x1p40f));
+    }
   }
 #pragma unroll
   for (int w = ITEMS; w > 1; w >>= 1)
@@ -258,7 +285,129 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
   z = (red[0] + red[1]) + (red[2] + red[3]);
   const float thr = p * z;
 
-  // bitonic sort of the keys, ascending
+  if (p_all || m_k >= nKV) {
+    // every block is kept
+    for (int w = tid; w < nwords; w += 256) {
+      const int rem = nKV - 32 * w;
+      bitmap[(size_t)row * nwords + w] = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
+    }
+    if (tid == 0) counts[row] = nKV;
+    return;
+  }
+
+  // smallest exponent-bin top set that provably holds the answer (wave 0; lane l looks at
+  // bins 127-2l and 126-2l, so lane order is descending bin order)
+  if (wid == 0) {
+    const int bh = 127 - 2 * lane, bl = 126 - 2 * lane;
+    const int ch = hist[bh], cl = hist[bl];
+    const unsigned long long mh = hmass[bh], ml = hmass[bl];
+    int ci = ch + cl;
+    unsigned long long mi = mh + ml;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int cy = __shfl_up(ci, o);
+      const unsigned long long my = __shfl_up(mi, o);
+      if (lane >= o) {
+        ci += cy;
+        mi += my;
+      }
+    }
+    const int ce = ci - (ch + cl);
+    const unsigned long long me = mi - (mh + ml);
+    const unsigned long long need =
+        (unsigned long long)ceil((double)thr * (1.0 + 1.0 / 1024.0) * 0x1p40);
+    const bool ok_h = (ce + ch >= m_k) && (me + mh >= need);
+    const bool ok_l = (ci >= m_k) && (mi >= need);
+    const unsigned long long bal_h = __ballot(ok_h), bal_l = __ballot(ok_l);
+    if (lane == 0) {
+      int bstar = 0;
+      if (bal_h | bal_l) {
+        const int fh = bal_h ? __ffsll((long long)bal_h) - 1 : 64;
+        const int fl = bal_l ? __ffsll((long long)bal_l) - 1 : 64;
+        if (fh <= fl) {
+          bstar = 127 - 2 * fh;
+        } else {
+          bstar = 126 - 2 * fl;
+        }
+      }
+      sh_bstar = bstar;
+      sh_pos = 0;
+    }
+    if (bal_h | bal_l) {
+      const int fh = bal_h ? __ffsll((long long)bal_h) - 1 : 64;
+      const int fl = bal_l ? __ffsll((long long)bal_l) - 1 : 64;
+      const int src = fh <= fl ? fh : fl;
+      const int cnt_h = __shfl(ce + ch, src), cnt_l = __shfl(ci, src);
+      if (lane == 0) sh_ncand = fh <= fl ? cnt_h : cnt_l;
+    } else if (lane == 0) {
+      sh_ncand = nKV;
+    }
+  }
+  __syncthreads();
+  const int bstar = sh_bstar;
+  const int ncand = sh_ncand;
+  int count;
+
+  if (ncand <= kCandCap) {
+    // candidates: blocks in bins >= bstar (a top set of the score order)
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int J = tid * ITEMS + i;
+      if (J < nKV && (int)(__float_as_uint(ev[J]) >> 23) >= bstar) {
+        const int pos = atomicAdd(&sh_pos, 1);
+        cand[pos] = kv[i];
+      }
+    }
+    __syncthreads();
+    // rank by counting (keys are distinct), scatter into score order
+    for (int c = tid; c < ncand; c += 256) {
+      const uint64_t k = cand[c];
+      int rank = 0;
+      for (int c2 = 0; c2 < ncand; ++c2) rank += cand[c2] < k ? 1 : 0;
+      csort[rank] = k;
+      cev[rank] = ev[(uint32_t)k];
+    }
+    __syncthreads();
+    if (wid == 0) {
+      int mp = -1;
+      float acc = 0.0f;
+      for (int c0 = 0; c0 < ncand; c0 += 64) {
+        const bool in = c0 + lane < ncand;
+        const int vbits = __float_as_int(in ? cev[c0 + lane] : 0.0f);
+        float pre = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+          acc = acc + __int_as_float(__builtin_amdgcn_readlane(vbits, u));
+          pre = (lane == u) ? acc : pre;
+        }
+        const unsigned long long hit = __ballot(in && pre >= thr);
+        if (hit != 0ull) {
+          mp = c0 + __ffsll((long long)hit);
+          break;
+        }
+      }
+      // no crossing inside a set that holds every block: no prefix reaches thr
+      if (mp < 0 && ncand == nKV) mp = nKV;
+      if (lane == 0) sh_count = mp < 0 ? -1 : max(m_k, mp);
+    }
+    __syncthreads();
+    count = sh_count;
+    if (count >= 0) {
+      for (int r = tid; r < count; r += 256) {
+        const uint32_t J = (uint32_t)csort[r];
+        atomicOr(&bits[J >> 5], 1u << (J & 31));
+      }
+      __syncthreads();
+      for (int w = tid; w < nwords; w += 256) bitmap[(size_t)row * nwords + w] = bits[w];
+      if (tid == 0) counts[row] = count;
+      return;
+    }
+  }
+
+  // full sort: bitonic sort of all keys, ascending
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) keys[tid * ITEMS + i] = kv[i];
+  __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < P / 2; i += 256) {
@@ -295,29 +444,27 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
   // is wave-uniform.
   if (wid == 0) {
     int mp = nKV;
-    if (!p_all) {
-      float acc = 0.0f;
-      for (int c0 = 0; c0 < nKV; c0 += 64) {
-        const bool in = c0 + lane < nKV;
-        const float val = in ? ev[c0 + lane] : 0.0f;
-        const int vbits = __float_as_int(val);
-        float pre = 0.0f;
+    float acc = 0.0f;
+    for (int c0 = 0; c0 < nKV; c0 += 64) {
+      const bool in = c0 + lane < nKV;
+      const float val = in ? ev[c0 + lane] : 0.0f;
+      const int vbits = __float_as_int(val);
+      float pre = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 64; ++u) {
-          acc = acc + __int_as_float(__builtin_amdgcn_readlane(vbits, u));
-          pre = (lane == u) ? acc : pre;
-        }
-        const unsigned long long hit = __ballot(in && pre >= thr);
-        if (hit != 0ull) {
-          mp = c0 + __ffsll((long long)hit);
-          break;
-        }
+      for (int u = 0; u < 64; ++u) {
+        acc = acc + __int_as_float(__builtin_amdgcn_readlane(vbits, u));
+        pre = (lane == u) ? acc : pre;
+      }
+      const unsigned long long hit = __ballot(in && pre >= thr);
+      if (hit != 0ull) {
+        mp = c0 + __ffsll((long long)hit);
+        break;
       }
     }
     if (lane == 0) sh_count = max(m_k, mp);
   }
   __syncthreads();
-  const int count = sh_count;
+  count = sh_count;
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {
     const int r = tid + q * 256;

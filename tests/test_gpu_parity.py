@@ -114,6 +114,22 @@ def test_tie_breaks_to_lower_block():
     assert 11 not in set(ci.tolist()) or 5 in set(ci.tolist())
 
 
+@pytest.mark.parametrize("scale", [0.0, 1e-3, 0.3])
+def test_plan_flat_and_near_flat_rows(scale):
+    """Near-uniform pooled scores over 1,100 KV blocks put more than 512 blocks into the
+    top exponent bin, so the router takes its full-sort path; a scale of 0 gives exact
+    ties everywhere (lowest block index first)."""
+    w = small_workload(f"flat{scale}", 1, 2, 64 * 1100, 64, "bf16", 128, 0.02, 0.9)
+    q, k, v, _ = W.make_inputs(w)
+    k32 = W.to_f32(k) * scale
+    kb = W.f64_to_bf16_bits(k32.astype(np.float64))
+    p = sa.plan(to_dev(q), to_dev(kb), w.block_q, w.block_kv, w.topk, w.top_p)
+    rp, ci, mp = oracle_plan(W.to_f32(q), W.to_f32(kb), w.block_q, w.block_kv, w.topk, w.top_p)
+    assert_same_csr(p.csr(), (rp, ci), f"flat {scale}")
+    if scale == 0.0:
+        assert np.all(np.diff(rp) == np.diff(rp)[0])
+
+
 def test_dense_plan_matches_dense_oracle():
     w = small_workload("dense", 1, 2, 1000, 128, "bf16", 128, 0.1, 0.9)
     ent = inputs(w)
