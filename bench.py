@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "attention.hip")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "sparse_fwd_bf16.hip")
 
 
 def log(msg):
@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--workload", default="wan14b_720p", choices=sorted(W.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -247,6 +249,15 @@ def main():
             "kernel": "sparse_fwd_kernel",
         },
     }
+    if args.copy_probe_mib > 0:
+        # a plain copy of known size: HBM counters of this kernel calibrate the others
+        nb = args.copy_probe_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = nb
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp, ci)
     print(json.dumps(out), flush=True)

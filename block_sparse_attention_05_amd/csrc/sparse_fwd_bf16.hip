@@ -65,19 +65,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
-  constexpr int GR = D / 8 + 1;             // 16-byte granules per LDS row (one pad granule)
-  constexpr int ROWB = GR * 16;             // bytes per LDS row
-  constexpr int NI = GR;                    // 1 KB direct loads per 64-row tile (64*GR/64)
-  constexpr int NIW = (NI + NW - 1) / NW;   // direct loads per wave and matrix
+  constexpr int GR = D / 8 + 1;             // K: 16-byte granules per LDS row (one pad granule)
+  constexpr int ROWB = GR * 16;             // K: bytes per LDS row
+  constexpr int NI = GR;                    // K: 1 KB direct loads per 64-row tile (64*GR/64)
+  constexpr int NIW = (NI + NW - 1) / NW;   // K: direct loads per wave
+  constexpr int VROWB = D * 2;              // V: unpadded rows, 64-byte segments XOR-swizzled
+  constexpr int VNI = D / 8;                // V: 1 KB direct loads per tile
+  constexpr int VNIW = (VNI + NW - 1) / NW;
+  constexpr int VSEG = D / 32;              // V: 64-byte segments per row (swizzle range)
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
 
   // double-buffered K and V tiles, row-major [key][channel] with padded rows; separate
   // arrays so the compiler can tell the in-flight loads from the tile being read
   __shared__ __align__(16) char k0s[kBk * ROWB];
-  __shared__ __align__(16) char v0s[kBk * ROWB];
+  __shared__ __align__(16) char v0s[kBk * VROWB];
   __shared__ __align__(16) char k1s[kBk * ROWB];
-  __shared__ __align__(16) char v1s[kBk * ROWB];
+  __shared__ __align__(16) char v1s[kBk * VROWB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,12 +139,22 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // Direct HBM -> LDS tile loads. Load i of a matrix fills LDS granules 64i .. 64i+63 of
   // the padded tile; lane p of it carries granule 64i + p = (row r, column granule c).
   // Pad granules (c == D/8) reload granule 0 of their row. Wave w issues loads w, w+NW, ...
-  int goff[NIW];      // byte offset of the lane's source granule within a 64-row tile
+  int goff[NIW];      // K: byte offset of the lane's source granule within a 64-row tile
 #pragma unroll
   for (int m = 0; m < NIW; ++m) {
     const int p = 64 * (wid + m * NW) + lane;
     const int c = p % GR;
     goff[m] = ((p / GR) * D + (c < D / 8 ? c : 0) * 8) * 2;
+  }
+  // V: LDS granule (row r, physical granule pg) holds logical granule
+  // pg ^ ((r mod VSEG) << 2), i.e. the 64-byte segments of a row are XOR-permuted by its
+  // row index; the four rows a transposing read touches then fall on disjoint bank ranges
+  int vgoff[VNIW];
+#pragma unroll
+  for (int m = 0; m < VNIW; ++m) {
+    const int P = 64 * (wid + m * NW) + lane;
+    const int r = P / (D / 8), pg = P % (D / 8);
+    vgoff[m] = (r * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
   }
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
   const int32_t *__restrict__ cols = a.col_idx + beg;
@@ -153,10 +167,14 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < NIW; ++m) {
         const int i = wid + m * NW;
-        if (i < NI) {
+        if (i < NI)
           __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + goff[m]), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
-        }
+      }
+#pragma unroll
+      for (int m = 0; m < VNIW; ++m) {
+        const int i = wid + m * NW;
+        if (i < VNI)
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + vgoff[m]), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
       }
     } else {
       // the ragged last block: rows past N reload the last valid row (in bounds, finite)
@@ -170,6 +188,15 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
           const int r = min(p / GR, last);
           const int off = (r * D + (c < D / 8 ? c : 0) * 8) * 2;
           __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + off), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < VNIW; ++m) {
+        const int i = wid + m * NW;
+        if (i < VNI) {
+          const int P = 64 * i + lane;
+          const int r = P / (D / 8), pg = P % (D / 8);
+          const int off = (min(r, last) * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
           __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + off), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
         }
       }
@@ -185,11 +212,16 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   float l_run = 0.0f;       // this lane's part of the running sum
   const float sl2 = a.scale_log2;
 
-  // per-lane LDS byte offsets: K operand row l32, granule hf; V^T operand source row
-  // (hf*4 + u/4), channel 16*(group & 1) + 4*(u & 3), u = lane & 15
+  // per-lane LDS byte offsets. K operand: row l32, granule hf. V^T operand source: row
+  // hf*4 + u/4 and channel 32t + 16*(group & 1) + 4*(u & 3) (u = lane & 15), whose 64-byte
+  // segment t sits at t ^ (u/4 mod VSEG) in the swizzled row
   const int koff = l32 * ROWB + hf * 16;
   const int u = lane & 15;
-  const int voff = (hf * 4 + (u >> 2)) * ROWB + (16 * ((lane >> 4) & 1) + 4 * (u & 3)) * 2;
+  int voff[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+    voff[t] = (hf * 4 + (u >> 2)) * VROWB + ((t ^ ((u >> 2) & (VSEG - 1))) * 64) +
+              (16 * ((lane >> 4) & 1) + 4 * (u & 3)) * 2;
 
   auto tile = [&](int J, const char *kt_s, const char *vt_s, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -258,9 +290,9 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kt][i0 + e];
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const char *p0 = vt_s + voff + base * ROWB + t * 64;
+        const char *p0 = vt_s + voff[t] + base * VROWB;
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(p0));
-        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(p0 + 8 * ROWB));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(p0 + 8 * VROWB));
         const bf16x8_t vw = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw, pb, oacc[t], 0, 0, 0);
       }
