@@ -33,6 +33,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -52,6 +53,7 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x4_t v;
   v[0] = (__bf16)a;
   v[1] = (__bf16)b;
@@ -85,7 +87,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -139,7 +141,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // Direct HBM -> LDS tile loads. Load i of a matrix fills LDS granules 64i .. 64i+63 of
   // the padded tile; lane p of it carries granule 64i + p = (row r, column granule c).
   // Pad granules (c == D/8) reload granule 0 of their row. Wave w issues loads w, w+NW, ...
-  int goff[NIW];      // K: byte offset of the lane's source granule within a 64-row tile
+  uint32_t goff[NIW]; // K: byte offset of the lane's source granule within a 64-row tile
 #pragma unroll
   for (int m = 0; m < NIW; ++m) {
     const int p = 64 * (wid + m * NW) + lane;
@@ -149,7 +151,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // V: LDS granule (row r, physical granule pg) holds logical granule
   // pg ^ ((r mod VSEG) << 2), i.e. the 64-byte segments of a row are XOR-permuted by its
   // row index; the four rows a transposing read touches then fall on disjoint bank ranges
-  int vgoff[VNIW];
+  uint32_t vgoff[VNIW];
 #pragma unroll
   for (int m = 0; m < VNIW; ++m) {
     const int P = 64 * (wid + m * NW) + lane;
@@ -186,7 +188,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
           const int p = 64 * i + lane;
           const int c = p % GR;
           const int r = min(p / GR, last);
-          const int off = (r * D + (c < D / 8 ? c : 0) * 8) * 2;
+          const uint32_t off = (r * D + (c < D / 8 ? c : 0) * 8) * 2;
           __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + off), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
         }
       }
@@ -196,7 +198,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
         if (i < VNI) {
           const int P = 64 * i + lane;
           const int r = P / (D / 8), pg = P % (D / 8);
-          const int off = (min(r, last) * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
+          const uint32_t off = (min(r, last) * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
           __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + off), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
         }
       }
@@ -209,7 +211,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[t][i] = 0.0f;
   float m_run = -INFINITY;  // running max, scaled logits, log2 domain
-  float l_run = 0.0f;       // this lane's part of the running sum
+  float lsum[2] = {0.0f, 0.0f};  // this lane's part of the running sum (two chains)
   const float sl2 = a.scale_log2;
 
   // per-lane LDS byte offsets. K operand: row l32, granule hf. V^T operand source: row
@@ -261,23 +263,18 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     if (__ballot(need)) {
       const float m_new = fmaxf(m_run, mt);
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= corr;
+      lsum[0] *= corr;
+      lsum[1] *= corr;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[t][i] *= corr;
       m_run = m_new;
     }
-    float psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[kt][i] * sl2 - m_run);
-        sacc[kt][i] = pv;
-        psum += pv;
-      }
-    l_run += psum;
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = __builtin_amdgcn_exp2f(sacc[kt][i] * sl2 - m_run);
     // O^T += V^T P^T. Reduction index hf*8 + e stands for key base + (e/4)*8 + hf*4 + e%4,
     // where the S^T layout left this lane's probabilities; the V^T operand comes from two
     // transposing LDS reads of keys base + hf*4 + 0..3 and base + 8 + hf*4 + 0..3.
@@ -288,6 +285,13 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       bf16x8_t pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kt][i0 + e];
+      // the running sum takes the rounded probabilities that the MFMA multiplies
+      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t pp = {pb[2 * e], pb[2 * e + 1]};
+        lsum[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum[e & 1], false);
+      }
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const char *p0 = vt_s + voff[t] + base * VROWB;
@@ -331,6 +335,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   }
 
   // epilogue: normalise (and blend), store bf16
+  const float l_run = lsum[0] + lsum[1];
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   if (q_ok) {
