@@ -87,12 +87,12 @@ sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP
 // Linear-branch workspace: per head H^T (bf16 [D, D]) and z (fp32 [D]), the per-chunk
 // partials of both (fp32), and the fp32 linear output Ol [B, H, N, D].
 struct FwdLayout {
-  size_t lin_ht, lin_z, partial, ol, total;
-  int chunks;
+  size_t lin_h, lin_z, partial, ol, phik, total;
+  int chunks, n_pad;
 };
 
 FwdLayout fwd_layout(const Shape &s, int with_linear) {
-  FwdLayout L{0, 0, 0, 0, 0, 0};
+  FwdLayout L{0, 0, 0, 0, 0, 0, 0, 0};
   if (!with_linear) return L;
   const size_t BH = (size_t)s.B * s.H;
   L.chunks = linear_prepass_chunks(s.N);
@@ -102,10 +102,12 @@ FwdLayout fwd_layout(const Shape &s, int with_linear) {
     off = align_up(off + bytes);
     return at;
   };
-  L.lin_ht = take(BH * s.D * s.D * 2);
+  L.n_pad = s.nKV * 64;
+  L.lin_h = take(BH * s.D * s.D * 4);
   L.lin_z = take(BH * s.D * 4);
   L.partial = take(BH * (size_t)L.chunks * s.D * (s.D + 1) * 4);
   L.ol = take(BH * (size_t)s.N * s.D * 4);
+  L.phik = take(BH * (size_t)L.n_pad * s.D * 2);
   L.total = off;
   return L;
 }
@@ -280,16 +282,19 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.ol = nullptr;
   if (alpha != nullptr) {
     char *ws = static_cast<char *>(workspace);
-    uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.lin_ht);
-    float *z = reinterpret_cast<float *>(ws + L.lin_z);
-    float *ol = reinterpret_cast<float *>(ws + L.ol);
-    hipError_t e = launch_linear_prepass(k, v, dtype, B * H, N, D,
-                                         reinterpret_cast<float *>(ws + L.partial), L.chunks, ht,
-                                         z, stream);
-    if (e == hipSuccess) e = launch_linear_apply(a, ht, z, ol, stream);
+    LinearBufs lb;
+    lb.partial = reinterpret_cast<float *>(ws + L.partial);
+    lb.chunks = L.chunks;
+    lb.phik = reinterpret_cast<uint16_t *>(ws + L.phik);
+    lb.n_pad = L.n_pad;
+    lb.h = reinterpret_cast<float *>(ws + L.lin_h);
+    lb.z = reinterpret_cast<float *>(ws + L.lin_z);
+    lb.ol = reinterpret_cast<float *>(ws + L.ol);
+    hipError_t e = launch_linear_prepass(k, v, dtype, B * H, N, D, lb, stream);
+    if (e == hipSuccess) e = launch_linear_apply(a, lb, stream);
     if (e != hipSuccess) return SA_ERR_HIP;
     a.alpha = alpha;
-    a.ol = ol;
+    a.ol = lb.ol;
   }
   return hip_status(launch_fwd(a, dtype, stream));
 }

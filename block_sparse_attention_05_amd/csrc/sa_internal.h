@@ -44,13 +44,22 @@ struct FwdArgs {
 };
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);  // sparse_fwd_bf16.hip
-// Linear branch (linear.hip): per-head H^T = sum_j v_j phi(k_j)^T (bf16 [B*H, D, D]) and
-// z = sum_j phi(k_j) (fp32 [B*H, D]); then Ol per query block over its masked-out blocks.
+// Linear branch (linear.hip). The prepass writes, per head, phi(k) in bf16 with zero rows
+// padding N up to a multiple of 64 ([B*H, n_pad, D]), H = sum_j phi(k_j) v_j^T (fp32
+// [B*H, D, D], row c = key channel, column d = value channel) and z = sum_j phi(k_j) (fp32
+// [B*H, D]); the apply step then writes Ol per query block over its masked-out blocks.
+struct LinearBufs {
+  float *partial;          // [B*H, chunks, D*D + D] per-chunk partial H and z
+  int chunks;
+  uint16_t *phik;          // [B*H, n_pad, D]
+  int n_pad;
+  float *h;                // [B*H, D, D]
+  float *z;                // [B*H, D]
+  float *ol;               // [B*H, N, D]
+};
 hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int BH, int N, int D,
-                                 float *partial, int n_chunks, uint16_t *lin_ht, float *lin_z,
-                                 hipStream_t s);
-hipError_t launch_linear_apply(const FwdArgs &a, const uint16_t *lin_ht, const float *lin_z,
-                               float *ol, hipStream_t s);
+                                 const LinearBufs &lb, hipStream_t s);
+hipError_t launch_linear_apply(const FwdArgs &a, const LinearBufs &lb, hipStream_t s);
 int linear_prepass_chunks(int N);
 
 }  // namespace sa
