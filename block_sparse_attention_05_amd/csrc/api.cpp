@@ -164,7 +164,7 @@ sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, 
   if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, stream);
   if (e == hipSuccess) e = launch_fill(bitmap, nwords, p.row_ptr, (int)s.R, p.col_idx, stream);
   if (e == hipSuccess)
-    e = launch_row_order(p.row_ptr, (int)s.R, s.nKV, p.row_order, counts, stream);
+    e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
   *out = p;
   return SA_OK;
@@ -184,9 +184,7 @@ sa_status sparse_attn_plan_dense(sa_dtype dtype, int B, int H, int N, int D, int
   fill_plan(&p, s, dtype, static_cast<char *>(workspace), L);
   hipError_t e = launch_dense_plan((int)s.R, s.nKV, p.row_ptr, p.col_idx, stream);
   if (e == hipSuccess)
-    e = launch_row_order(p.row_ptr, (int)s.R, s.nKV, p.row_order,
-                         reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + L.counts),
-                         stream);
+    e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
   *out = p;
   return SA_OK;
@@ -228,8 +226,7 @@ sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, 
   // the host arrays may be pageable and reused as soon as this call returns
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e == hipSuccess)
-    e = launch_row_order(p.row_ptr, (int)s.R, s.nKV, p.row_order,
-                         reinterpret_cast<int32_t *>(ws + L.counts), stream);
+    e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
   *out = p;
   return SA_OK;

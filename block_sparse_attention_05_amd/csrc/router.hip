@@ -20,6 +20,7 @@
 // Pooling per block and per head follows the SLA2 page, router item 1.
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "sa_internal.h"
@@ -558,9 +559,110 @@ __global__ void dense_plan_kernel(int R, int nKV, int32_t *__restrict__ row_ptr,
   if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[R] = (int32_t)total;
 }
 
-__global__ void identity_order_kernel(int R, int32_t *__restrict__ row_order) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < R) row_order[i] = i;
+// Work order for the forward kernels. A forward launch of R workgroups runs workgroup b
+// on XCD b mod 8 and gives it slot (b mod 8) * q + b / 8 (q = R / 8; slots from 8q on
+// map to themselves), so XCD x works through slots [x q, (x+1) q) in order. Rows are
+// dealt to the XCDs in runs of consecutive rows (chunks) aligned to heads: whole heads,
+// or each head cut into k equal runs when there are fewer than 32 heads, or g whole
+// heads per run when there are more than kOrderMaxChunks. Chunks go by descending
+// kept-tile total, each to the XCD with the least work so far that still has free slots,
+// split where an XCD fills up; an XCD runs its runs in that order (heaviest first) and
+// each run in ascending row order. A head's
+// query blocks keep many KV blocks in common, so keeping a head's rows together on one
+// XCD keeps its L2 reuse, while the per-XCD totals come out nearly equal.
+constexpr int kOrderMaxChunks = 512;
+
+__device__ __forceinline__ void order_chunk(int c, int nQ, int BH, int k, int g, int M, int *start, int *len) {
+  int s, e;
+  if (g > 1) {
+    s = c * g * nQ;
+    e = min(BH, (c + 1) * g) * nQ;
+  } else {
+    const int h = c / k, j = c - (c / k) * k;
+    s = h * nQ + (j * nQ) / k;
+    e = h * nQ + ((j + 1) * nQ) / k;
+  }
+  s = min(s, M);
+  e = min(e, M);
+  *start = s;
+  *len = e - s;
+}
+
+__global__ __launch_bounds__(256) void balance_order_kernel(const int32_t *__restrict__ row_ptr, int R, int nQ,
+                                                            int32_t *__restrict__ row_order) {
+  __shared__ int ch_work[kOrderMaxChunks], ch_start[kOrderMaxChunks], ch_len[kOrderMaxChunks];
+  __shared__ int4 sorted[kOrderMaxChunks];               // (work, start, len, -)
+  __shared__ int pc_start[kOrderMaxChunks + 8], pc_len[kOrderMaxChunks + 8], pc_off[kOrderMaxChunks + 8];
+  __shared__ int n_pieces;
+  const int tid = threadIdx.x;
+  const int q = R / 8;
+  const int M = 8 * q;
+  for (int s = M + tid; s < R; s += 256) row_order[s] = s;
+  if (q == 0) return;
+  const int BH = R / nQ;
+  const int k = BH >= 32 ? 1 : min(nQ, ceil_div(32, BH));
+  const int g = BH > kOrderMaxChunks ? ceil_div(BH, kOrderMaxChunks) : 1;
+  const int nch = g > 1 ? ceil_div(BH, g) : BH * k;
+  for (int c = tid; c < nch; c += 256) {
+    int st, ln;
+    order_chunk(c, nQ, BH, k, g, M, &st, &ln);
+    ch_start[c] = st;
+    ch_len[c] = ln;
+    ch_work[c] = row_ptr[st + ln] - row_ptr[st];
+  }
+  __syncthreads();
+  // rank by (work descending, index ascending)
+  for (int c = tid; c < nch; c += 256) {
+    const int wc = ch_work[c];
+    int r = 0;
+    for (int c2 = 0; c2 < nch; ++c2) {
+      const int w2 = ch_work[c2];
+      r += (w2 > wc) || (w2 == wc && c2 < c);
+    }
+    sorted[r] = make_int4(wc, ch_start[c], ch_len[c], 0);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int load[8], cap[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      load[x] = 0;
+      cap[x] = q;
+    }
+    int np = 0;
+    for (int i = 0; i < nch; ++i) {
+      const int4 ch = sorted[i];
+      int start = ch.y, len = ch.z;
+      while (len > 0) {
+        int x = 0, best = cap[0] > 0 ? load[0] : INT_MAX;
+#pragma unroll
+        for (int y = 1; y < 8; ++y) {
+          const int ly = cap[y] > 0 ? load[y] : INT_MAX;
+          if (ly < best) {
+            best = ly;
+            x = y;
+          }
+        }
+        const int take = min(len, cap[x]);
+        pc_off[np] = x * q + (q - cap[x]);  // runs fill an XCD's slots in assignment order
+        pc_start[np] = start;
+        pc_len[np] = take;
+        ++np;
+        // a split chunk's work is shared pro rata (rounded down per row)
+        load[x] += take == ch.z ? ch.x : (ch.x / ch.z) * take;
+        cap[x] -= take;
+        start += take;
+        len -= take;
+      }
+    }
+    n_pieces = np;
+  }
+  __syncthreads();
+  const int np = n_pieces;
+  for (int p = tid >> 6; p < np; p += 4) {  // one wave per run
+    const int base = pc_off[p], st = pc_start[p], ln = pc_len[p];
+    for (int i = tid & 63; i < ln; i += 64) row_order[base + i] = st + i;
+  }
 }
 
 __global__ void router_exp_kernel(const float *__restrict__ x, float *__restrict__ y, int64_t n) {
@@ -634,12 +736,8 @@ hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx,
   return hipGetLastError();
 }
 
-hipError_t launch_row_order(const int32_t *row_ptr, int R, int nKV, int32_t *row_order,
-                            int32_t *scratch, hipStream_t s) {
-  (void)row_ptr;
-  (void)nKV;
-  (void)scratch;
-  identity_order_kernel<<<ceil_div(R, 256), 256, 0, s>>>(R, row_order);
+hipError_t launch_row_order(const int32_t *row_ptr, int R, int nQ, int32_t *row_order, hipStream_t s) {
+  balance_order_kernel<<<1, 256, 0, s>>>(row_ptr, R, nQ, row_order);
   return hipGetLastError();
 }
 

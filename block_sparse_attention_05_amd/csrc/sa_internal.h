@@ -12,7 +12,7 @@ constexpr int kMaxKvBlocks = 4096;
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Router launchers (router.hip). All return hipSuccess or the launch error.
 hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int N, int D, int bs, float *out,
@@ -25,8 +25,7 @@ hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, hipStream
 hipError_t launch_fill(const uint32_t *bitmap, int nwords, const int32_t *row_ptr, int R,
                        int32_t *col_idx, hipStream_t s);
 hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
-hipError_t launch_row_order(const int32_t *row_ptr, int R, int nKV, int32_t *row_order,
-                            int32_t *scratch, hipStream_t s);
+hipError_t launch_row_order(const int32_t *row_ptr, int R, int nQ, int32_t *row_order, hipStream_t s);
 hipError_t launch_router_exp(const float *x, float *y, int64_t n, hipStream_t s);
 
 // Attention launchers (attention.hip).

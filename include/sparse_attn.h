@@ -71,7 +71,10 @@ typedef struct sa_plan {
   int32_t reserved;
   int32_t *row_ptr;          /* device, [R + 1], row_ptr[0] = 0, row_ptr[R] = nnz */
   int32_t *col_idx;          /* device, capacity R * n_kvblk; ascending within a row */
-  int32_t *row_order;        /* device, [R]: rows by descending kept count (work order) */
+  int32_t *row_order;        /* device, [R]: a permutation of the rows, the order in which
+                              * the forward kernels visit them (runs of consecutive rows
+                              * spread so that each XCD gets an equal kept-tile share);
+                              * it changes no result */
 } sa_plan;
 
 /* Accepted shapes: D in {64, 128}; block_q in {64, 128}; block_kv = 64; B*H <= 65535;

@@ -299,3 +299,82 @@ def test_workload_dense_sampled(name, nrows):
         want.append(ob)
     mx, rr = check_out(np.concatenate(got), np.concatenate(want), "bf16", name + " dense")
     log(f"{name} dense: sampled {len(rows)} rows max|dO| {mx:.2e} rel-RMS {rr:.2e}")
+
+
+# ------------------------------------------------------------------ work order
+def order_chunks(R, nQ):
+    """Runs of consecutive rows the work order deals out: whole heads, each head cut into
+    k equal runs when there are fewer than 32 heads, or g heads per run beyond 512 runs."""
+    M = 8 * (R // 8)
+    BH = R // nQ
+    k = 1 if BH >= 32 else min(nQ, -(-32 // BH))
+    g = -(-BH // 512) if BH > 512 else 1
+    out = []
+    if g > 1:
+        for c in range(-(-BH // g)):
+            out.append((c * g * nQ, min(BH, (c + 1) * g) * nQ))
+    else:
+        for h in range(BH):
+            for j in range(k):
+                out.append((h * nQ + j * nQ // k, h * nQ + (j + 1) * nQ // k))
+    return [(min(s, M), min(e, M) - min(s, M)) for s, e in out]
+
+
+def balanced_order_reference(rp, nQ):
+    """Host restatement of the plan's work order: head-aligned runs of consecutive rows
+    dealt to the eight XCD slot ranges, heaviest run first, each to the least-loaded
+    range with room (a run that does not fit is split); a range holds its runs in the
+    order they were dealt."""
+    R = rp.size - 1
+    q = R // 8
+    order = np.arange(R, dtype=np.int64)
+    if q == 0:
+        return order
+    chunks = order_chunks(R, nQ)
+    work = [int(rp[s + n] - rp[s]) for s, n in chunks]
+    ranked = sorted(range(len(chunks)), key=lambda c: (-work[c], c))
+    load, cap = [0] * 8, [q] * 8
+    for c in ranked:
+        start, ln = chunks[c]
+        len0 = ln
+        while ln > 0:
+            x = min((y for y in range(8) if cap[y] > 0), key=lambda y: (load[y], y))
+            take = min(ln, cap[x])
+            off = x * q + (q - cap[x])
+            order[off:off + take] = np.arange(start, start + take)
+            load[x] += work[c] if take == len0 else (work[c] // len0) * take
+            cap[x] -= take
+            start += take
+            ln -= take
+    return order
+
+
+@pytest.mark.parametrize("name", ["wan14b_720p", "wan13b_480p"])
+def test_row_order_balanced(name):
+    w = W.CONFIGS[name]
+    ent = inputs(w)
+    p, (rp, _) = gpu_plan(w, ent)
+    got = p.row_order().cpu().numpy().astype(np.int64)
+    R = rp.size - 1
+    assert np.array_equal(np.sort(got), np.arange(R)), "not a permutation"
+    ref = balanced_order_reference(rp, w.n_qblk)
+    assert np.array_equal(got, ref)
+    q = R // 8
+    cnt = np.diff(rp)
+    tot = np.array([cnt[got[x * q:(x + 1) * q]].sum() for x in range(8)])
+    log(f"{name}: per-XCD kept tiles {tot.tolist()}, max/mean {tot.max() / tot.mean():.4f}")
+    heaviest = max(rp[s + n] - rp[s] for s, n in order_chunks(R, w.n_qblk))
+    assert tot.max() <= tot.mean() + heaviest
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[2], SMALL[7]], ids=["tiny_like", "ragged_q128", "nkv300"])
+def test_row_order_small(case):
+    w = small_workload(*case)
+    ent = inputs(w)
+    p, (rp, _) = gpu_plan(w, ent)
+    got = p.row_order().cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, balanced_order_reference(rp, w.n_qblk))
+    pd = sa.plan_dense(ent["dq"], w.block_q, w.block_kv)
+    rpd = pd.row_ptr().cpu().numpy().astype(np.int64)
+    assert np.array_equal(pd.row_order().cpu().numpy().astype(np.int64),
+                          balanced_order_reference(rpd, w.n_qblk))
