@@ -119,7 +119,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan14b_720p", choices=sorted(W.CONFIGS))
+    ap.add_argument("--workload", default="wan14b_720p", choices=sorted(W.CONFIGS) + sorted(W.SWEEP))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -133,7 +133,7 @@ def main():
     import torch
     import block_sparse_attention_05_amd as sa
 
-    w = W.CONFIGS[args.workload]
+    w = W.CONFIGS[args.workload] if args.workload in W.CONFIGS else W.SWEEP[args.workload]
     t0 = time.time()
     q, k, v, alpha = W.make_inputs(w)
     log(f"inputs {w.name}: B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype} in {time.time() - t0:.1f}s")

@@ -107,6 +107,10 @@ def long_sweep() -> List[Workload]:
     return [LONG_245K.replace(name=f"long_T{t}", grid=(t, 64, 64)) for t in (8, 15, 30, 60)]
 
 
+# the sweep points are also addressable by name (T = 60 is long_245k itself)
+SWEEP: Dict[str, Workload] = {w.name: w for w in long_sweep()}
+
+
 def _rng(*key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
 
