@@ -233,6 +233,11 @@ def main():
         },
         "ms_plan": round(t_plan, 4),
         "ms_fwd": round(t_fwd, 4),
+        "ms_step_median": round(float(np.median(ms_step)), 4),
+        "ms_step_min": round(float(np.min(ms_step)), 4),
+        "ms_plan_median": round(float(np.median(ms_plan)), 4),
+        "ms_fwd_median": round(float(np.median(ms_fwd)), 4),
+        "ms_fwd_min": round(float(np.min(ms_fwd)), 4),
         "fwd_tflops": round(achieved, 2),
         "kept_pairs": pairs,
         "nnz_tiles": nnz,
@@ -246,7 +251,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": "sparse_fwd_kernel",
+            "kernel": "sparse_fwd_bf16_kernel" if w.dtype == "bf16" else "sparse_fwd_kernel",
         },
     }
     if args.copy_probe_mib > 0:
