@@ -18,6 +18,9 @@ Two tracks:
   dense attention, a brute-force N x N masked softmax, and the elu+1 linear branch over
   the masked-out blocks blended as O = alpha*Os + (1 - alpha)*Ol (SLA2 page, item 2;
   SALAD page, section 2.1).
+* ``oracle.heatmap``: the ground-truth tile heatmap of full attention (Veda page,
+  section 2.1: max pooling of the attention matrix over query x key tiles), and the
+  mean attention mass per tile, in float64.
 
 Parity pins (tests marked "not gpu") tie both tracks to facts outside the oracle:
 closed forms, library routines, brute force and hand-derived fixtures. Parity of the
@@ -28,10 +31,11 @@ from .mask import (exp_sa, pool_blocks, block_scores, tree_sum, select_row, topk
                    oracle_plan, plan_stats, score_scale)
 from .attention import (sparse_attention, dense_attention, brute_masked_attention,
                         linear_branch, blend, phi, dense_plan, csr_to_mask)
+from .heatmap import tile_heatmap
 
 __all__ = [
     "exp_sa", "pool_blocks", "block_scores", "tree_sum", "select_row", "topk_count",
     "oracle_plan", "plan_stats", "score_scale",
     "sparse_attention", "dense_attention", "brute_masked_attention", "linear_branch",
-    "blend", "phi", "dense_plan", "csr_to_mask",
+    "blend", "phi", "dense_plan", "csr_to_mask", "tile_heatmap",
 ]
