@@ -24,7 +24,8 @@ SA_BF16, SA_FP32 = 0, 1
 EXPORTS = (
     "sparse_attn_plan_workspace_bytes", "sparse_attn_plan", "sparse_attn_plan_dense",
     "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
-    "sparse_attn_router_exp", "sparse_attn_status_string", "sparse_attn_version",
+    "sparse_attn_tile_stats", "sparse_attn_router_exp", "sparse_attn_status_string",
+    "sparse_attn_version",
 )
 
 
@@ -70,6 +71,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_fwd_workspace_bytes.restype = sz
     lib.sparse_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd.restype = i32
+    lib.sparse_attn_tile_stats.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [vp, vp, vp]
+    lib.sparse_attn_tile_stats.restype = i32
     lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
     lib.sparse_attn_router_exp.restype = i32
     lib.sparse_attn_status_string.argtypes = [i32]
@@ -258,6 +261,26 @@ def fwd(q, k, v, plan: Plan, alpha=None, return_lse: bool = False, out=None, lse
                                ws.numel() if ws is not None else 0, _stream(stream)),
            "sparse_attn_fwd")
     return (o, lse) if return_lse else o
+
+
+def tile_stats(q, k, lse, block_q: int = 128, block_kv: int = 64, stream=None):
+    """Pass 2 of the ground-truth tile heatmap (see sparse_attn_tile_stats): returns
+    (tile_max, tile_mass), float32 [B*H*n_qblk, n_kvblk], from q, k [B, H, N, D] bf16 and
+    lse [B, H, N] (fwd on plan_dense with return_lse)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k)
+    B, H, N, D = q.shape
+    if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+            and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] GPU tensor")
+    nq, nkv = -(-N // block_q), -(-N // block_kv)
+    tmax = torch.empty((B * H * nq, nkv), dtype=torch.float32, device=q.device)
+    tmass = torch.empty_like(tmax)
+    _check(lib.sparse_attn_tile_stats(q.data_ptr(), k.data_ptr(), lse.data_ptr(), _dtype_code(q),
+                                      B, H, N, D, block_q, block_kv, tmax.data_ptr(),
+                                      tmass.data_ptr(), _stream(stream)), "sparse_attn_tile_stats")
+    return tmax, tmass
 
 
 def router_exp(x, stream=None):

@@ -29,6 +29,7 @@ SOURCES = {
     "attention.hip": [],
     "sparse_fwd_bf16.hip": [],
     "linear.hip": [],
+    "heatmap.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

@@ -296,6 +296,21 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   return hip_status(launch_fwd(a, dtype, stream));
 }
 
+sa_status sparse_attn_tile_stats(const void *q, const void *k, const float *lse, sa_dtype dtype,
+                                 int B, int H, int N, int D, int block_q, int block_kv,
+                                 float *tile_max, float *tile_mass, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || lse == nullptr) return SA_ERR_INVALID_ARG;
+  if (tile_max == nullptr && tile_mass == nullptr) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  const sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
+  if (st != SA_OK) return st;
+  if (dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
+  return hip_status(launch_tile_stats(q, k, lse, B * H, H, N, D, s.bq, s.nQ, s.nKV, sl2, tile_max,
+                                      tile_mass, stream));
+}
+
 sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (x == nullptr || y == nullptr))) return SA_ERR_INVALID_ARG;
   if (n == 0) return SA_OK;

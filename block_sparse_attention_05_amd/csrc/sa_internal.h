@@ -60,5 +60,8 @@ hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int 
                                  const LinearBufs &lb, hipStream_t s);
 hipError_t launch_linear_apply(const FwdArgs &a, const LinearBufs &lb, hipStream_t s);
 int linear_prepass_chunks(int N);
+// Tile heatmap, pass 2 (heatmap.hip): per (row, KV block) max and mean mass of exp(s - lse).
+hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
+                             int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s);
 
 }  // namespace sa

@@ -130,6 +130,21 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
                           const float *alpha, void *o, float *lse,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Ground-truth tile heatmap of full attention (Veda page, section 2.1: the reference mask
+ * max-pools the full attention matrix over query x key tiles; section 2.3: two passes).
+ * Pass 1 is sparse_attn_fwd on a sparse_attn_plan_dense plan with an lse output; this
+ * call is pass 2. With p_ij = exp(q_i.k_j / sqrt(D) - lse_i), for every row
+ * r = (b*H + h)*n_qblk + I and KV block J:
+ *   tile_max[r*n_kvblk + J]  = max of p_ij over i in query block I, j in KV block J;
+ *   tile_mass[r*n_kvblk + J] = the sum of those p_ij divided by the size of block I.
+ * q, k: device [B, H, N, D] bf16 (fp32 inputs return SA_ERR_UNSUPPORTED).
+ * lse: device float [B, H, N], finite, natural log (as sparse_attn_fwd writes it).
+ * tile_max, tile_mass: device float [B*H*n_qblk*n_kvblk]; either may be NULL, not both.
+ * Shapes and block sizes are checked as for sparse_attn_plan. Deterministic. */
+sa_status sparse_attn_tile_stats(const void *q, const void *k, const float *lse, sa_dtype dtype,
+                                 int B, int H, int N, int D, int block_q, int block_kv,
+                                 float *tile_max, float *tile_mass, hipStream_t stream);
+
 /* Diagnostic: y[i] = the router's fp32 exp of x[i] for x[i] <= 0 (0 below -86), evaluated
  * on the device with the router's own code. x, y: device float [n]. */
 sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream);

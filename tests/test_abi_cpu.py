@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 9
+    assert len(decl) == 10
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -140,3 +140,23 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         sa.plan(q, q, 64, 64)
+
+
+def test_tile_stats_validation(lib):
+    """Every invalid tile-heatmap call is rejected on the host (nothing is launched)."""
+    E = B
+    f = lib.sparse_attn_tile_stats
+
+    def call(q=FAKE, k=FAKE, lse=FAKE, dt=0, shape=(1, 2, 1024, 64, 64, 64), tmax=FAKE, tmass=FAKE):
+        return f(q, k, lse, dt, *shape, tmax, tmass, None)
+
+    assert call(q=None) == E.SA_ERR_INVALID_ARG
+    assert call(k=None) == E.SA_ERR_INVALID_ARG
+    assert call(lse=None) == E.SA_ERR_INVALID_ARG
+    assert call(tmax=None, tmass=None) == E.SA_ERR_INVALID_ARG
+    assert call(dt=5) == E.SA_ERR_INVALID_ARG
+    assert call(dt=1) == E.SA_ERR_UNSUPPORTED                     # fp32 inputs
+    assert call(shape=(1, 2, 0, 64, 64, 64)) == E.SA_ERR_INVALID_ARG
+    assert call(shape=(1, 2, 1024, 96, 64, 64)) == E.SA_ERR_UNSUPPORTED
+    assert call(shape=(1, 2, 1024, 64, 64, 128)) == E.SA_ERR_UNSUPPORTED
+    assert call(shape=(1, 1, 64 * 4097, 64, 64, 64)) == E.SA_ERR_UNSUPPORTED
