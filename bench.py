@@ -52,6 +52,43 @@ def kept_flops(rp: np.ndarray, ci: np.ndarray, w: W.Workload) -> float:
     return 4.0 * w.D * pairs, pairs
 
 
+def mask_quality(tmax: np.ndarray, tmass: np.ndarray, rp: np.ndarray, ci: np.ndarray) -> dict:
+    """How well a block mask (CSR rp, ci) matches the ground-truth tile heatmap of full
+    attention (tile max and mean mass per row, [R, nKV]). Per row with n kept tiles:
+      recall_max   share of the n kept tiles among the n tiles with the largest max
+      recall_mass  the same against the n tiles with the largest mass
+      retained     attention mass on the kept tiles (of 1 per query)
+      efficiency   retained / the largest mass any n tiles of the row hold
+    Ties rank the lower block index first. Returns means and a few percentiles."""
+    R, nkv = tmax.shape
+    counts = np.diff(rp).astype(np.int64)
+    kept = np.zeros((R, nkv), dtype=bool)
+    kept[np.repeat(np.arange(R), counts), ci] = True
+    idx = np.arange(nkv)[None, :]
+
+    def top_n(score):
+        order = np.argsort(-score, axis=1, kind="stable")
+        rank = np.empty_like(order)
+        np.put_along_axis(rank, order, np.broadcast_to(idx, order.shape), axis=1)
+        return rank < counts[:, None]
+
+    tmax_top = top_n(tmax)
+    tmass_top = top_n(tmass)
+    n = np.maximum(counts, 1)
+    recall_max = (kept & tmax_top).sum(axis=1) / n
+    recall_mass = (kept & tmass_top).sum(axis=1) / n
+    retained = np.where(kept, tmass, 0.0).sum(axis=1)
+    best = np.where(tmass_top, tmass, 0.0).sum(axis=1)
+    eff = retained / np.maximum(best, 1e-30)
+
+    def stats(x):
+        return {"mean": round(float(x.mean()), 4), "p10": round(float(np.percentile(x, 10)), 4),
+                "min": round(float(x.min()), 4)}
+
+    return {"rows": int(R), "recall_max": stats(recall_max), "recall_mass": stats(recall_mass),
+            "retained_mass": stats(retained), "mass_efficiency": stats(eff)}
+
+
 def source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -122,6 +159,9 @@ def main():
     ap.add_argument("--workload", default="wan14b_720p", choices=sorted(W.CONFIGS) + sorted(W.SWEEP))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--quality", action="store_true",
+                    help="also build the ground-truth tile heatmap of full attention (two "
+                         "passes) and report the router mask's recall and retained mass")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -263,6 +303,27 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_probe_bytes"] = nb
+    if args.quality:
+        if w.dtype != "bf16":
+            raise SystemExit("--quality needs a bf16 workload")
+        pd = sa.plan_dense(dq, w.block_q, w.block_kv)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        sa.fwd(dq, dk, dv, pd, return_lse=True, out=o, lse=lse)
+        tmax, tmass = sa.tile_stats(dq, dk, lse, w.block_q, w.block_kv)
+        e[0].record(stream)
+        sa.fwd(dq, dk, dv, pd, return_lse=True, out=o, lse=lse)
+        e[1].record(stream)
+        tmax, tmass = sa.tile_stats(dq, dk, lse, w.block_q, w.block_kv)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        t2 = e[1].elapsed_time(e[2])
+        qual = mask_quality(tmax.cpu().numpy(), tmass.cpu().numpy(), rp, ci)
+        qual["ms_pass1_dense_fwd_lse"] = round(e[0].elapsed_time(e[1]), 3)
+        qual["ms_pass2_tile_stats"] = round(t2, 3)
+        qual["pass2_tflops"] = round(2.0 * w.D * w.B * w.H * float(w.N) * w.N / t2 / 1e9, 1)
+        out["quality"] = qual
+        del pd, lse, tmax, tmass
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp, ci)
     print(json.dumps(out), flush=True)

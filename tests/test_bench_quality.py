@@ -1,0 +1,30 @@
+"""The mask-quality measurement (recall and retained mass of a block mask against a tile
+heatmap) on hand-made rows."""
+import numpy as np
+
+import bench
+
+
+def test_mask_quality_hand_rows():
+    tmax = np.array([[0.9, 0.1, 0.5, 0.2],
+                     [0.1, 0.2, 0.3, 0.4]])
+    tmass = np.array([[0.6, 0.1, 0.2, 0.1],
+                      [0.1, 0.2, 0.3, 0.4]])
+    # row 0 keeps blocks {0, 1}; row 1 keeps {3}
+    rp = np.array([0, 2, 3])
+    ci = np.array([0, 1, 3])
+    q = bench.mask_quality(tmax, tmass, rp, ci)
+    # row 0: top-2 by max is {0, 2} -> recall 1/2; by mass {0, 2} -> 1/2;
+    # retained 0.7 of a best 0.8. Row 1: top-1 is {3} -> recall 1, retained 0.4 of 0.4.
+    assert q["recall_max"]["mean"] == 0.75 and q["recall_max"]["min"] == 0.5
+    assert q["recall_mass"]["mean"] == 0.75
+    assert abs(q["retained_mass"]["mean"] - 0.55) < 1e-9
+    assert abs(q["mass_efficiency"]["min"] - 0.875) < 1e-4
+
+
+def test_mask_quality_ties_rank_lower_index_first():
+    tmax = np.array([[0.5, 0.5, 0.5]])
+    tmass = np.array([[0.3, 0.3, 0.4]])
+    q = bench.mask_quality(tmax, tmass, np.array([0, 1]), np.array([0]))
+    assert q["recall_max"]["mean"] == 1.0      # block 0 wins the three-way tie
+    assert q["recall_mass"]["mean"] == 0.0     # block 2 holds the most mass
