@@ -630,8 +630,10 @@ __global__ __launch_bounds__(256) void balance_order_kernel(const int32_t *__res
       cap[x] = q;
     }
     int np = 0;
+    int4 next = sorted[0];
     for (int i = 0; i < nch; ++i) {
-      const int4 ch = sorted[i];
+      const int4 ch = next;
+      if (i + 1 < nch) next = sorted[i + 1];   // the next chunk's LDS read overlaps this one
       int start = ch.y, len = ch.z;
       while (len > 0) {
         int x = 0, best = cap[0] > 0 ? load[0] : INT_MAX;
