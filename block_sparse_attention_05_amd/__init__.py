@@ -8,16 +8,20 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
     plan_dense(q, ...), plan_from_csr(q, ...)   all-ones and caller-given masks
     tile_stats(q, k, lse, ...)                  ground-truth tile heatmap (max and mean
                                                 mass of full attention per tile)
+    cube_permute(x, grid, cubes, inverse)       head-aware 3-D tiling: raster <-> per-head
+                                                cube order of the tokens
 
 All computation happens in the library's HIP kernels; torch supplies device memory and
 streams.
 """
-from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, fwd, load_library,
+from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, cube_permute, fwd,
+                       load_library,
                        plan, plan_dense, plan_from_csr, plan_workspace_bytes, router_exp, tile_stats,
                        version)
 
 __all__ = [
-    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "fwd", "load_library",
+    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "cube_permute", "fwd",
+    "load_library",
     "plan", "plan_dense", "plan_from_csr", "plan_workspace_bytes", "router_exp", "tile_stats",
     "version",
 ]

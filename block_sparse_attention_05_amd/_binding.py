@@ -24,8 +24,8 @@ SA_BF16, SA_FP32 = 0, 1
 EXPORTS = (
     "sparse_attn_plan_workspace_bytes", "sparse_attn_plan", "sparse_attn_plan_dense",
     "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
-    "sparse_attn_tile_stats", "sparse_attn_router_exp", "sparse_attn_status_string",
-    "sparse_attn_version",
+    "sparse_attn_tile_stats", "sparse_attn_cube_permute", "sparse_attn_router_exp",
+    "sparse_attn_status_string", "sparse_attn_version",
 )
 
 
@@ -73,6 +73,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_fwd.restype = i32
     lib.sparse_attn_tile_stats.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [vp, vp, vp]
     lib.sparse_attn_tile_stats.restype = i32
+    lib.sparse_attn_cube_permute.argtypes = [vp, vp, i32] + [i32] * 7 + [vp, i32, vp]
+    lib.sparse_attn_cube_permute.restype = i32
     lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
     lib.sparse_attn_router_exp.restype = i32
     lib.sparse_attn_status_string.argtypes = [i32]
@@ -281,6 +283,26 @@ def tile_stats(q, k, lse, block_q: int = 128, block_kv: int = 64, stream=None):
                                       B, H, N, D, block_q, block_kv, tmax.data_ptr(),
                                       tmass.data_ptr(), _stream(stream)), "sparse_attn_tile_stats")
     return tmax, tmass
+
+
+def cube_permute(x, grid, cubes, inverse: bool = False, out=None, stream=None):
+    """Moves each head's tokens of x [B, H, N, D] (raster order on the (T, Hg, W) grid)
+    into the cube order of cubes[h] = (ct, ch, cw), or back with inverse=True (see
+    sparse_attn_cube_permute). Returns the moved tensor."""
+    torch = _torch()
+    lib = load_library()
+    if not (x.is_cuda and x.is_contiguous() and x.dim() == 4):
+        raise ValueError("x must be a contiguous [B, H, N, D] GPU tensor")
+    B, H, N, D = x.shape
+    cub = np.ascontiguousarray(np.asarray(cubes, dtype=np.int32).reshape(-1))
+    if cub.size != 3 * H:
+        raise ValueError("cubes must give (ct, ch, cw) for every head")
+    o = out if out is not None else torch.empty_like(x)
+    T, Hg, W = (int(g) for g in grid)
+    _check(lib.sparse_attn_cube_permute(x.data_ptr(), o.data_ptr(), _dtype_code(x), B, H, N, D, T, Hg,
+                                        W, cub.ctypes.data, 1 if inverse else 0, _stream(stream)),
+           "sparse_attn_cube_permute")
+    return o
 
 
 def router_exp(x, stream=None):

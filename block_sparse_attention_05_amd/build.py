@@ -30,6 +30,7 @@ SOURCES = {
     "sparse_fwd_bf16.hip": [],
     "linear.hip": [],
     "heatmap.hip": [],
+    "tiling.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

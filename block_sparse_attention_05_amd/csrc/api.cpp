@@ -311,6 +311,29 @@ sa_status sparse_attn_tile_stats(const void *q, const void *k, const float *lse,
                                       tile_mass, stream));
 }
 
+sa_status sparse_attn_cube_permute(const void *src, void *dst, sa_dtype dtype, int B, int H, int N,
+                                   int D, int T, int Hg, int W, const int32_t *host_cubes,
+                                   int inverse, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || host_cubes == nullptr) return SA_ERR_INVALID_ARG;
+  if (src == dst) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || T <= 0 || Hg <= 0 || W <= 0) return SA_ERR_INVALID_ARG;
+  if (inverse != 0 && inverse != 1) return SA_ERR_INVALID_ARG;
+  if ((long)T * Hg * W != (long)N) return SA_ERR_INVALID_ARG;
+  const int eb = dtype == SA_BF16 ? 2 : 4;
+  if ((D * eb) % 16 != 0 || D > 4096) return SA_ERR_UNSUPPORTED;
+  if (H > kMaxCubeHeads || (long)B * H > 65535) return SA_ERR_UNSUPPORTED;
+  if ((long)N * (D * eb / 16) >= (1L << 31)) return SA_ERR_UNSUPPORTED;
+  CubeTable cubes{};
+  for (int h = 0; h < H; ++h)
+    for (int a = 0; a < 3; ++a) {
+      const int c = host_cubes[h * 3 + a];
+      if (c < 1) return SA_ERR_INVALID_ARG;
+      cubes.c[h][a] = c;
+    }
+  return hip_status(launch_cube_permute(src, dst, B * H, H, N, D * eb, T, Hg, W, cubes, inverse, stream));
+}
+
 sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (x == nullptr || y == nullptr))) return SA_ERR_INVALID_ARG;
   if (n == 0) return SA_OK;

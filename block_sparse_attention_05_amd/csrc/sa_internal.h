@@ -60,6 +60,13 @@ hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int 
                                  const LinearBufs &lb, hipStream_t s);
 hipError_t launch_linear_apply(const FwdArgs &a, const LinearBufs &lb, hipStream_t s);
 int linear_prepass_chunks(int N);
+// Head-aware 3-D tiling (tiling.hip): raster <-> per-head cube order of [B, H, N, D] rows.
+constexpr int kMaxCubeHeads = 128;
+struct CubeTable {
+  int c[kMaxCubeHeads][3];   // (ct, ch, cw) per head
+};
+hipError_t launch_cube_permute(const void *src, void *dst, int BH, int H, int N, int row_bytes, int T,
+                               int Hg, int W, const CubeTable &cubes, int inverse, hipStream_t s);
 // Tile heatmap, pass 2 (heatmap.hip): per (row, KV block) max and mean mass of exp(s - lse).
 hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
                              int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s);

@@ -145,6 +145,22 @@ sa_status sparse_attn_tile_stats(const void *q, const void *k, const float *lse,
                                  int B, int H, int N, int D, int block_q, int block_kv,
                                  float *tile_max, float *tile_mass, hipStream_t stream);
 
+/* Head-aware 3-D tiling (Veda page, section 2.2: each head tiles the token grid with its
+ * own factorisation of the hardware tile, so that a block of consecutive tokens is a
+ * compact spatio-temporal cube). Tokens lie on a (T, Hg, W) grid in raster order,
+ * n = (t*Hg + y)*W + x, N = T*Hg*W. Head h's cube order with cube (ct, ch, cw) sorts the
+ * tokens by (t/ct, y/ch, x/cw, t%ct, y%ch, x%cw); pos_h(n) is token n's place in it.
+ * inverse = 0: dst[b, h, pos_h(n), :] = src[b, h, n, :] (raster to cube order);
+ * inverse = 1: dst[b, h, n, :] = src[b, h, pos_h(n), :] (back to raster order).
+ * Attention on cube-ordered q, k, v (plan and fwd as usual, with the blocks now cubes)
+ * followed by the inverse move of o is attention under the cube partition.
+ * src, dst: device [B, H, N, D] in dtype, not overlapping; D*element size a multiple of
+ * 16 bytes. host_cubes: host int32 [H*3], (ct, ch, cw) per head, each >= 1; H <= 128.
+ * Bitwise copy; no arithmetic on the values. */
+sa_status sparse_attn_cube_permute(const void *src, void *dst, sa_dtype dtype, int B, int H, int N,
+                                   int D, int T, int Hg, int W, const int32_t *host_cubes,
+                                   int inverse, hipStream_t stream);
+
 /* Diagnostic: y[i] = the router's fp32 exp of x[i] for x[i] <= 0 (0 below -86), evaluated
  * on the device with the router's own code. x, y: device float [n]. */
 sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream);

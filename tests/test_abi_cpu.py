@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 10
+    assert len(decl) == 11
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -160,3 +160,26 @@ def test_tile_stats_validation(lib):
     assert call(shape=(1, 2, 1024, 96, 64, 64)) == E.SA_ERR_UNSUPPORTED
     assert call(shape=(1, 2, 1024, 64, 64, 128)) == E.SA_ERR_UNSUPPORTED
     assert call(shape=(1, 1, 64 * 4097, 64, 64, 64)) == E.SA_ERR_UNSUPPORTED
+
+
+def test_cube_permute_validation(lib):
+    """Every invalid cube-permutation call is rejected on the host (nothing is launched)."""
+    E = B
+    f = lib.sparse_attn_cube_permute
+    good = np.array([2, 4, 16] * 2, dtype=np.int32)
+
+    def call(src=FAKE, dst=FAKE + 4096, dt=0, shape=(1, 2, 21 * 45 * 80, 128), grid=(21, 45, 80),
+             cubes=good, inv=0):
+        c = np.ascontiguousarray(cubes, dtype=np.int32)
+        return f(src, dst, dt, *shape, *grid, c.ctypes.data if c.size else None, inv, None)
+
+    assert call(src=None) == E.SA_ERR_INVALID_ARG
+    assert call(dst=None) == E.SA_ERR_INVALID_ARG
+    assert call(dst=FAKE) == E.SA_ERR_INVALID_ARG                    # in place
+    assert call(cubes=np.zeros(0)) == E.SA_ERR_INVALID_ARG
+    assert call(dt=3) == E.SA_ERR_INVALID_ARG
+    assert call(inv=2) == E.SA_ERR_INVALID_ARG
+    assert call(grid=(21, 45, 79)) == E.SA_ERR_INVALID_ARG          # T*Hg*W != N
+    assert call(cubes=np.array([2, 0, 16, 1, 1, 1])) == E.SA_ERR_INVALID_ARG
+    assert call(shape=(1, 2, 21 * 45 * 80, 4)) == E.SA_ERR_UNSUPPORTED   # rows of 8 bytes
+    assert call(shape=(1, 129, 21 * 45 * 80, 128), cubes=np.ones(129 * 3)) == E.SA_ERR_UNSUPPORTED
