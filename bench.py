@@ -33,6 +33,9 @@ METRIC = "sparse-attn ms/call + effective TFLOP/s (kept tiles) vs bf16 MFMA peak
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
 HBM_PEAK_GBS = 8000.0
+# head-aware 3-D tiling (--cubes): (t, h, w) extents, cycled over the heads
+Q_CUBES = [(2, 4, 16), (1, 8, 16), (4, 4, 8)]
+KV_CUBES = [(1, 4, 16), (2, 4, 8), (4, 4, 4)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "sparse_fwd_bf16.hip")
 
@@ -159,6 +162,10 @@ def main():
     ap.add_argument("--workload", default="wan14b_720p", choices=sorted(W.CONFIGS) + sorted(W.SWEEP))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cubes", action="store_true",
+                    help="head-aware 3-D tiling: put each head's tokens in a cube order "
+                         "(per-head cubes cycled from a fixed list) before the plan and "
+                         "move the output back after the forward; both moves are timed")
     ap.add_argument("--quality", action="store_true",
                     help="also build the ground-truth tile heatmap of full attention (two "
                          "passes) and report the router mask's recall and retained mass")
@@ -186,14 +193,39 @@ def main():
     dq, dk, dv = dev(q), dev(k), dev(v)
     dalpha = dev(alpha) if w.linear else None
     stream = torch.cuda.current_stream()
+    raw = (dq, dk, dv)
+    qc = kc = q_table = None
+    if args.cubes:
+        # fixed per-head cubes (no search): t x h x w extents of 128 (query) and 64 (key).
+        # K and V are moved into cube order; q is read, and o written, in raster order
+        # through the plan's query-order table (built once, like the cube shapes).
+        qc = [Q_CUBES[h % len(Q_CUBES)] for h in range(w.H)]
+        kc = [KV_CUBES[h % len(KV_CUBES)] for h in range(w.H)]
+        q_table = sa.cube_order(w.H, w.grid, qc)
+        dk, dv = torch.empty_like(dk), torch.empty_like(dv)
+
+    def move_in():
+        if qc is not None:
+            sa.cube_permute(raw[1], w.grid, kc, out=dk)
+            sa.cube_permute(raw[2], w.grid, kc, out=dv)
+
+    def move_out():
+        pass
+
+    def make_plan():
+        if q_table is not None:
+            return sa.plan_ordered(dq, dk, q_table, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        return sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
     ws = torch.empty(sa.plan_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty_like(dq)
 
     def step():
-        p = sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        move_in()
+        p = make_plan()
         ev_mid.record(stream)
         sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
+        move_out()
         return p
 
     ev_mid = torch.cuda.Event(enable_timing=True)
@@ -207,17 +239,24 @@ def main():
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    moved = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    fwd_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
         starts[i].record(stream)
-        p = sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        move_in()
+        moved[i].record(stream)
+        p = make_plan()
         mids[i].record(stream)
         sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
+        fwd_end[i].record(stream)
+        move_out()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_plan = [s.elapsed_time(m) for s, m in zip(starts, mids)]
-    ms_fwd = [m.elapsed_time(e) for m, e in zip(mids, ends)]
+    ms_plan = [s.elapsed_time(m) for s, m in zip(moved, mids)]
+    ms_fwd = [m.elapsed_time(e) for m, e in zip(mids, fwd_end)]
+    ms_move = [a.elapsed_time(b) + c.elapsed_time(d) for a, b, c, d in zip(starts, moved, fwd_end, ends)]
     t_step = float(np.mean(ms_step))
     t_fwd = float(np.mean(ms_fwd))
     t_plan = float(np.mean(ms_plan))
@@ -270,6 +309,9 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "grid": list(w.grid),
             "block_q": w.block_q, "block_kv": w.block_kv, "topk": w.topk, "top_p": w.top_p,
             "linear_branch": bool(w.linear),
+            "cube_tiling": ({"query_cubes": Q_CUBES, "key_cubes": KV_CUBES, "per_head": "h mod 3",
+                             "moved": "k, v (q and o through the plan's query order)"}
+                            if args.cubes else None),
         },
         "ms_plan": round(t_plan, 4),
         "ms_fwd": round(t_fwd, 4),
@@ -278,6 +320,7 @@ def main():
         "ms_plan_median": round(float(np.median(ms_plan)), 4),
         "ms_fwd_median": round(float(np.median(ms_fwd)), 4),
         "ms_fwd_min": round(float(np.min(ms_fwd)), 4),
+        **({"ms_cube_moves": round(float(np.mean(ms_move)), 4)} if args.cubes else {}),
         "fwd_tflops": round(achieved, 2),
         "kept_pairs": pairs,
         "nnz_tiles": nnz,
@@ -306,15 +349,17 @@ def main():
     if args.quality:
         if w.dtype != "bf16":
             raise SystemExit("--quality needs a bf16 workload")
-        pd = sa.plan_dense(dq, w.block_q, w.block_kv)
+        # the heatmap's query blocks must be the plan's rows: cube-ordered q under --cubes
+        hq = sa.cube_permute(raw[0], w.grid, qc) if qc is not None else dq
+        pd = sa.plan_dense(hq, w.block_q, w.block_kv)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        sa.fwd(dq, dk, dv, pd, return_lse=True, out=o, lse=lse)
-        tmax, tmass = sa.tile_stats(dq, dk, lse, w.block_q, w.block_kv)
+        sa.fwd(hq, dk, dv, pd, return_lse=True, out=o, lse=lse)
+        tmax, tmass = sa.tile_stats(hq, dk, lse, w.block_q, w.block_kv)
         e[0].record(stream)
-        sa.fwd(dq, dk, dv, pd, return_lse=True, out=o, lse=lse)
+        sa.fwd(hq, dk, dv, pd, return_lse=True, out=o, lse=lse)
         e[1].record(stream)
-        tmax, tmass = sa.tile_stats(dq, dk, lse, w.block_q, w.block_kv)
+        tmax, tmass = sa.tile_stats(hq, dk, lse, w.block_q, w.block_kv)
         e[2].record(stream)
         torch.cuda.synchronize()
         t2 = e[1].elapsed_time(e[2])
@@ -323,9 +368,16 @@ def main():
         qual["ms_pass2_tile_stats"] = round(t2, 3)
         qual["pass2_tflops"] = round(2.0 * w.D * w.B * w.H * float(w.N) * w.N / t2 / 1e9, 1)
         out["quality"] = qual
-        del pd, lse, tmax, tmass
+        del pd, lse, tmax, tmass, hq
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp, ci)
+        if qc is not None:
+            # the oracle on the same cube-ordered head 0 as the plan's CSR describes
+            from oracle import permute_heads
+            out["cpu_baseline"] = cpu_baseline(w, permute_heads(q[:, :1], w.grid, qc[:1]),
+                                               permute_heads(k[:, :1], w.grid, kc[:1]),
+                                               permute_heads(v[:, :1], w.grid, kc[:1]), rp, ci)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp, ci)
     print(json.dumps(out), flush=True)
 
 

@@ -10,18 +10,21 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
                                                 mass of full attention per tile)
     cube_permute(x, grid, cubes, inverse)       head-aware 3-D tiling: raster <-> per-head
                                                 cube order of the tokens
+    cube_order(H, grid, cubes)                  the same order as a table, and
+    plan_ordered(q, k, q_order, ...)            a mask whose query blocks follow it
+                                                (q and o stay in raster order)
 
 All computation happens in the library's HIP kernels; torch supplies device memory and
 streams.
 """
-from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, cube_permute, fwd,
-                       load_library,
+from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, cube_order,
+                       cube_permute, fwd, load_library, plan_ordered,
                        plan, plan_dense, plan_from_csr, plan_workspace_bytes, router_exp, tile_stats,
                        version)
 
 __all__ = [
-    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "cube_permute", "fwd",
-    "load_library",
+    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "cube_order",
+    "cube_permute", "fwd", "load_library", "plan_ordered",
     "plan", "plan_dense", "plan_from_csr", "plan_workspace_bytes", "router_exp", "tile_stats",
     "version",
 ]

@@ -24,8 +24,9 @@ SA_BF16, SA_FP32 = 0, 1
 EXPORTS = (
     "sparse_attn_plan_workspace_bytes", "sparse_attn_plan", "sparse_attn_plan_dense",
     "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
-    "sparse_attn_tile_stats", "sparse_attn_cube_permute", "sparse_attn_router_exp",
-    "sparse_attn_status_string", "sparse_attn_version",
+    "sparse_attn_plan_ordered", "sparse_attn_tile_stats", "sparse_attn_cube_permute",
+    "sparse_attn_cube_order", "sparse_attn_router_exp", "sparse_attn_status_string",
+    "sparse_attn_version",
 )
 
 
@@ -36,6 +37,7 @@ class SaPlan(ctypes.Structure):
         ("n_qblk", ctypes.c_int32), ("n_kvblk", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("row_order", ctypes.c_void_p),
+        ("q_order", ctypes.c_void_p),
     ]
 
 
@@ -63,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_plan_workspace_bytes.restype = sz
     lib.sparse_attn_plan.argtypes = [vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, sz, pplan, vp]
     lib.sparse_attn_plan.restype = i32
+    lib.sparse_attn_plan_ordered.argtypes = [vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, vp, sz, pplan, vp]
+    lib.sparse_attn_plan_ordered.restype = i32
     lib.sparse_attn_plan_dense.argtypes = [i32] * 7 + [vp, sz, pplan, vp]
     lib.sparse_attn_plan_dense.restype = i32
     lib.sparse_attn_plan_from_csr.argtypes = [i32] * 7 + [vp, vp, vp, sz, pplan, vp]
@@ -75,6 +79,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_tile_stats.restype = i32
     lib.sparse_attn_cube_permute.argtypes = [vp, vp, i32] + [i32] * 7 + [vp, i32, vp]
     lib.sparse_attn_cube_permute.restype = i32
+    lib.sparse_attn_cube_order.argtypes = [i32] * 4 + [vp, vp, vp]
+    lib.sparse_attn_cube_order.restype = i32
     lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
     lib.sparse_attn_router_exp.restype = i32
     lib.sparse_attn_status_string.argtypes = [i32]
@@ -134,9 +140,10 @@ def _check_qkv(*ts):
 class Plan:
     """A block mask in CSR form living in a torch-owned workspace on the GPU."""
 
-    def __init__(self, ws, st: SaPlan):
+    def __init__(self, ws, st: SaPlan, keep=None):
         self.ws = ws          # keeps the workspace (and so the CSR arrays) alive
         self.st = st
+        self.keep = keep      # keeps a caller table the plan points to (the query order) alive
 
     @property
     def shape(self) -> Tuple[int, int, int, int]:
@@ -200,6 +207,46 @@ def plan(q, k, block_q: int = 128, block_kv: int = 64, topk: float = 0.05, top_p
                                 block_kv, float(topk), float(top_p), ws.data_ptr(), ws.numel(),
                                 ctypes.byref(st), _stream(stream)), "sparse_attn_plan")
     return Plan(ws, st)
+
+
+def plan_ordered(q, k, q_order, block_q: int = 128, block_kv: int = 64, topk: float = 0.05,
+                 top_p: float = 0.9, stream=None, workspace=None) -> Plan:
+    """The mask for queries taken per head in the order q_order (int32 [H, N] GPU tensor,
+    position -> storage row; see sparse_attn_plan_ordered). q stays in storage order, k
+    (and the v later given to fwd) are in KV-block order; fwd with this plan writes o in
+    q's storage order."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k)
+    B, H, N, D = q.shape
+    if not (q_order.is_cuda and q_order.dtype == torch.int32 and q_order.is_contiguous()
+            and q_order.numel() == H * N):
+        raise ValueError("q_order must be a contiguous int32 [H, N] GPU tensor")
+    need = lib.sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "plan shape")
+    ws = workspace if workspace is not None else _new_ws(need, q.device)
+    st = SaPlan()
+    _check(lib.sparse_attn_plan_ordered(q.data_ptr(), k.data_ptr(), _dtype_code(q), B, H, N, D,
+                                        block_q, block_kv, float(topk), float(top_p),
+                                        q_order.data_ptr(), ws.data_ptr(), ws.numel(),
+                                        ctypes.byref(st), _stream(stream)), "sparse_attn_plan_ordered")
+    return Plan(ws, st, keep=q_order)
+
+
+def cube_order(H: int, grid, cubes, device="cuda", stream=None):
+    """Per-head cube orders as a table for plan_ordered: int32 [H, N] with
+    order[h, pos_h(n)] = n (see sparse_attn_cube_order)."""
+    torch = _torch()
+    lib = load_library()
+    T, Hg, W = (int(g) for g in grid)
+    cub = np.ascontiguousarray(np.asarray(cubes, dtype=np.int32).reshape(-1))
+    if cub.size != 3 * H:
+        raise ValueError("cubes must give (ct, ch, cw) for every head")
+    out = torch.empty((H, T * Hg * W), dtype=torch.int32, device=device)
+    _check(lib.sparse_attn_cube_order(H, T, Hg, W, cub.ctypes.data, out.data_ptr(), _stream(stream)),
+           "sparse_attn_cube_order")
+    return out
 
 
 def plan_dense(q, block_q: int = 128, block_kv: int = 64, stream=None) -> Plan:

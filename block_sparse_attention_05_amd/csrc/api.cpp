@@ -80,6 +80,7 @@ void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L
   p->row_ptr = reinterpret_cast<int32_t *>(ws + L.row_ptr);
   p->col_idx = reinterpret_cast<int32_t *>(ws + L.col_idx);
   p->row_order = reinterpret_cast<int32_t *>(ws + L.row_order);
+  p->q_order = nullptr;
 }
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
@@ -122,9 +123,11 @@ size_t sparse_attn_plan_workspace_bytes(int B, int H, int N, int D, int block_q,
   return plan_layout(s).total;
 }
 
-sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, int H, int N,
-                           int D, int block_q, int block_kv, double topk_frac, double top_p,
-                           void *workspace, size_t ws_bytes, sa_plan *out, hipStream_t stream) {
+namespace {
+sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, int N, int D,
+                    int block_q, int block_kv, double topk_frac, double top_p,
+                    const int32_t *q_order, void *workspace, size_t ws_bytes, sa_plan *out,
+                    hipStream_t stream) {
   if (q == nullptr || k == nullptr || out == nullptr) return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
   if (!(topk_frac >= 0.0 && topk_frac <= 1.0)) return SA_ERR_INVALID_ARG;
@@ -156,8 +159,9 @@ sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, 
   const int BH = B * H;
   const int nwords = ceil_div(s.nKV, 32);
 
-  hipError_t e = launch_pool(q, dtype, BH, N, D, block_q, qbar, stream);
-  if (e == hipSuccess) e = launch_pool(k, dtype, BH, N, D, block_kv, kbar, stream);
+  p.q_order = q_order;
+  hipError_t e = launch_pool(q, dtype, BH, H, N, D, block_q, q_order, qbar, stream);
+  if (e == hipSuccess) e = launch_pool(k, dtype, BH, H, N, D, block_kv, nullptr, kbar, stream);
   if (e == hipSuccess) e = launch_scores(qbar, kbar, BH, s.nQ, s.nKV, D, c, scores, stream);
   if (e == hipSuccess)
     e = launch_select(scores, (int)s.R, s.nKV, m_k, p32, p_all, bitmap, nwords, counts, stream);
@@ -168,6 +172,24 @@ sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, 
   if (e != hipSuccess) return SA_ERR_HIP;
   *out = p;
   return SA_OK;
+}
+}  // namespace
+
+sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, int H, int N,
+                           int D, int block_q, int block_kv, double topk_frac, double top_p,
+                           void *workspace, size_t ws_bytes, sa_plan *out, hipStream_t stream) {
+  return plan_impl(q, k, dtype, B, H, N, D, block_q, block_kv, topk_frac, top_p, nullptr,
+                   workspace, ws_bytes, out, stream);
+}
+
+sa_status sparse_attn_plan_ordered(const void *q, const void *k, sa_dtype dtype, int B, int H,
+                                   int N, int D, int block_q, int block_kv, double topk_frac,
+                                   double top_p, const int32_t *q_order, void *workspace,
+                                   size_t ws_bytes, sa_plan *out, hipStream_t stream) {
+  if (q_order == nullptr) return SA_ERR_INVALID_ARG;
+  if (dtype == SA_FP32) return SA_ERR_UNSUPPORTED;
+  return plan_impl(q, k, dtype, B, H, N, D, block_q, block_kv, topk_frac, top_p, q_order,
+                   workspace, ws_bytes, out, stream);
 }
 
 sa_status sparse_attn_plan_dense(sa_dtype dtype, int B, int H, int N, int D, int block_q,
@@ -265,6 +287,8 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.row_ptr = plan->row_ptr;
   a.col_idx = plan->col_idx;
   a.row_order = plan->row_order;
+  a.q_order = plan->q_order;
+  if (a.q_order != nullptr && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   a.B = B;
   a.H = H;
   a.N = N;
@@ -332,6 +356,22 @@ sa_status sparse_attn_cube_permute(const void *src, void *dst, sa_dtype dtype, i
       cubes.c[h][a] = c;
     }
   return hip_status(launch_cube_permute(src, dst, B * H, H, N, D * eb, T, Hg, W, cubes, inverse, stream));
+}
+
+sa_status sparse_attn_cube_order(int H, int T, int Hg, int W, const int32_t *host_cubes,
+                                 int32_t *order, hipStream_t stream) {
+  if (host_cubes == nullptr || order == nullptr) return SA_ERR_INVALID_ARG;
+  if (H <= 0 || T <= 0 || Hg <= 0 || W <= 0) return SA_ERR_INVALID_ARG;
+  if (H > kMaxCubeHeads) return SA_ERR_UNSUPPORTED;
+  if ((long)T * Hg * W * H >= (1L << 31)) return SA_ERR_UNSUPPORTED;
+  CubeTable cubes{};
+  for (int h = 0; h < H; ++h)
+    for (int a = 0; a < 3; ++a) {
+      const int c = host_cubes[h * 3 + a];
+      if (c < 1) return SA_ERR_INVALID_ARG;
+      cubes.c[h][a] = c;
+    }
+  return hip_status(launch_cube_order(H, T, Hg, W, cubes, order, stream));
 }
 
 sa_status sparse_attn_router_exp(const float *x, float *y, int64_t n, hipStream_t stream) {

@@ -270,13 +270,15 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
 
   // raw q of this wave's final-product query group, loaded early
   const int g = wid % QG;
-  const int qi = I * BQ + g * 32 + l32;
+  const int qi = I * BQ + g * 32 + l32;   // query position (Ol is written by position)
   const bool q_ok = qi < N;
+  int qrow = qi;                          // storage row of q
+  if (a.q_order && q_ok) qrow = min(max(a.q_order[(size_t)(bh % a.H) * N + qi], 0), N - 1);
   uint4 qraw[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     qraw[s] = make_uint4(0, 0, 0, 0);
-    if (q_ok) qraw[s] = *reinterpret_cast<const uint4 *>(qg + (size_t)qi * D + s * 16 + hf * 8);
+    if (q_ok) qraw[s] = *reinterpret_cast<const uint4 *>(qg + (size_t)qrow * D + s * 16 + hf * 8);
   }
 
   // tile list: the kept tiles (subtract) or the complement (direct sum); both fit in

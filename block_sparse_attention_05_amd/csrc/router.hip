@@ -69,9 +69,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // ---------------------------------------------------------------- pooling
 // One thread owns 8 channels of one block and walks its tokens in order; D/8 threads
 // cover a block row, so each token row is read as contiguous 16-byte pieces.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int N, int bs,
+// With ORD, block positions are mapped to storage rows through a per-head table (clamped
+// into [0, N)); the sum still runs over the block's positions in ascending order.
+template <typename T, int D, bool ORD>
+__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int H, int N, int bs,
                                                    int nblk, long total_blocks,
+                                                   const int32_t *__restrict__ order,
                                                    float *__restrict__ out) {
   constexpr int kTpb = D / 8;
   constexpr int kBlocksPerWg = 256 / kTpb;
@@ -84,13 +87,17 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
   const int t0 = I * bs;
   const int cnt = min(bs, N - t0);
   const T *p = x + ((size_t)bh * N + t0) * D + lane * 8;
+  const T *base = x + (size_t)bh * N * D + lane * 8;
+  const int32_t *ord = ORD ? order + (size_t)(bh % H) * N + t0 : nullptr;
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 #pragma unroll 8
   for (int t = 0; t < cnt; ++t) {
+    const T *rowp = p + (size_t)t * D;
+    if constexpr (ORD) rowp = base + (size_t)min(max(ord[t], 0), N - 1) * D;
     if constexpr (sizeof(T) == 2) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(p + (size_t)t * D);
+      const uint4 w = *reinterpret_cast<const uint4 *>(rowp);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -98,8 +105,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
         acc[2 * c + 1] = acc[2 * c + 1] + __uint_as_float(ws[c] & 0xffff0000u);
       }
     } else {
-      const float4 a = *reinterpret_cast<const float4 *>(p + (size_t)t * D);
-      const float4 b = *reinterpret_cast<const float4 *>(p + (size_t)t * D + 4);
+      const float4 a = *reinterpret_cast<const float4 *>(rowp);
+      const float4 b = *reinterpret_cast<const float4 *>(rowp + 4);
       acc[0] = acc[0] + a.x; acc[1] = acc[1] + a.y; acc[2] = acc[2] + a.z; acc[3] = acc[3] + a.w;
       acc[4] = acc[4] + b.x; acc[5] = acc[5] + b.y; acc[6] = acc[6] + b.z; acc[7] = acc[7] + b.w;
     }
@@ -676,23 +683,25 @@ __global__ void router_exp_kernel(const float *__restrict__ x, float *__restrict
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int N, int D, int bs, float *out,
-                       hipStream_t s) {
+hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int H, int N, int D, int bs,
+                       const int32_t *order, float *out, hipStream_t s) {
   const int nblk = ceil_div(N, bs);
   const long total = (long)BH * nblk;
   const int per_wg = 256 / (D / 8);
   const unsigned grid = (unsigned)((total + per_wg - 1) / per_wg);
+#define SA_POOL(T, DD, O)                                                                       \
+  pool_kernel<T, DD, O><<<grid, 256, 0, s>>>((const T *)x, H, N, bs, nblk, total, order, out)
   if (dt == SA_BF16) {
-    if (D == 128)
-      pool_kernel<uint16_t, 128><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);
-    else
-      pool_kernel<uint16_t, 64><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);
+    if (D == 128) {
+      if (order) SA_POOL(uint16_t, 128, true); else SA_POOL(uint16_t, 128, false);
+    } else {
+      if (order) SA_POOL(uint16_t, 64, true); else SA_POOL(uint16_t, 64, false);
+    }
   } else {
-    if (D == 128)
-      pool_kernel<float, 128><<<grid, 256, 0, s>>>((const float *)x, N, bs, nblk, total, out);
-    else
-      pool_kernel<float, 64><<<grid, 256, 0, s>>>((const float *)x, N, bs, nblk, total, out);
+    if (D == 128) SA_POOL(float, 128, false);
+    else SA_POOL(float, 64, false);
   }
+#undef SA_POOL
   return hipGetLastError();
 }
 

@@ -15,8 +15,9 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Router launchers (router.hip). All return hipSuccess or the launch error.
-hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int N, int D, int bs, float *out,
-                       hipStream_t s);
+// q_order: NULL, or per-head position -> row table; block rows are then read through it
+hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int H, int N, int D, int bs,
+                       const int32_t *order, float *out, hipStream_t s);
 hipError_t launch_scores(const float *qbar, const float *kbar, int BH, int nQ, int nKV, int D,
                          float c, float *scores, hipStream_t s);
 hipError_t launch_select(const float *scores, int R, int nKV, int m_k, float p, int p_all,
@@ -34,6 +35,7 @@ struct FwdArgs {
   void *o;
   float *lse;
   const int32_t *row_ptr, *col_idx, *row_order;
+  const int32_t *q_order;  // NULL, or per head: query position -> storage row of q, o, lse
   int B, H, N, D, block_q, block_kv, n_qblk, n_kvblk;
   float scale_log2;        // log2(e) / sqrt(D)
   double scale_log2_f64;   // the same in fp64
@@ -67,6 +69,8 @@ struct CubeTable {
 };
 hipError_t launch_cube_permute(const void *src, void *dst, int BH, int H, int N, int row_bytes, int T,
                                int Hg, int W, const CubeTable &cubes, int inverse, hipStream_t s);
+hipError_t launch_cube_order(int H, int T, int Hg, int W, const CubeTable &cubes, int32_t *order,
+                             hipStream_t s);
 // Tile heatmap, pass 2 (heatmap.hip): per (row, KV block) max and mean mass of exp(s - lse).
 hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
                              int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s);

@@ -103,8 +103,11 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   const uint16_t *vg = reinterpret_cast<const uint16_t *>(a.v) + head;
   uint16_t *og = reinterpret_cast<uint16_t *>(a.o) + head;
 
-  const int qi = I * BQ + wid * 32 + l32;
+  const int qi = I * BQ + wid * 32 + l32;   // query position
   const bool q_ok = qi < N;
+  // storage row of this query's q, o and lse (positions map through the plan's table)
+  int qrow = qi;
+  if (a.q_order && q_ok) qrow = min(max(a.q_order[(size_t)(bh % a.H) * N + qi], 0), N - 1);
   const int beg = a.row_ptr[row];
   const int end = a.row_ptr[row + 1];
 
@@ -122,9 +125,9 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
           o2 = (1.f - al.z) * lv.z;
           o3 = (1.f - al.w) * lv.w;
         }
-        *reinterpret_cast<uint2 *>(og + (size_t)qi * D + d) = pack4(o0, o1, o2, o3);
+        *reinterpret_cast<uint2 *>(og + (size_t)qrow * D + d) = pack4(o0, o1, o2, o3);
       }
-      if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = -INFINITY;
+      if (a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = -INFINITY;
     }
     return;
   }
@@ -134,7 +137,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (q_ok) w = *reinterpret_cast<const uint4 *>(qg + (size_t)qi * D + s * 16 + hf * 8);
+    if (q_ok) w = *reinterpret_cast<const uint4 *>(qg + (size_t)qrow * D + s * 16 + hf * 8);
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
   }
 
@@ -339,7 +342,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   if (q_ok) {
-    uint16_t *orow = og + (size_t)qi * D;
+    uint16_t *orow = og + (size_t)qrow * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -359,7 +362,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
         }
         *reinterpret_cast<uint2 *>(orow + d) = pack4(o0, o1, o2, o3);
       }
-    if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+    if (a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 

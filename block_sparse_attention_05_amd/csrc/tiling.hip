@@ -48,7 +48,25 @@ __global__ __launch_bounds__(256) void cube_permute_kernel(const uint4 *__restri
     dst[head + (size_t)p * G + g] = src[head + (size_t)n * G + g];
 }
 
+// order[h*N + pos_h(n)] = n, grid (ceil(N / 256), H)
+__global__ __launch_bounds__(256) void cube_order_kernel(int N, int T, int Hg, int W, CubeTable cubes,
+                                                         int32_t *__restrict__ order) {
+  const int h = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int p = cube_pos(n, T, Hg, W, cubes.c[h][0], cubes.c[h][1], cubes.c[h][2]);
+  order[(size_t)h * N + p] = n;
+}
+
 }  // namespace
+
+hipError_t launch_cube_order(int H, int T, int Hg, int W, const CubeTable &cubes, int32_t *order,
+                             hipStream_t s) {
+  const int N = T * Hg * W;
+  dim3 grid((unsigned)ceil_div(N, 256), H);
+  cube_order_kernel<<<grid, 256, 0, s>>>(N, T, Hg, W, cubes, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_cube_permute(const void *src, void *dst, int BH, int H, int N, int row_bytes, int T,
                                int Hg, int W, const CubeTable &cubes, int inverse, hipStream_t s) {

@@ -75,6 +75,9 @@ typedef struct sa_plan {
                               * the forward kernels visit them (runs of consecutive rows
                               * spread so that each XCD gets an equal kept-tile share);
                               * it changes no result */
+  const int32_t *q_order;    /* device [H*N] or NULL (caller-owned, see
+                              * sparse_attn_plan_ordered): query position i of head h is
+                              * raster token q_order[h*N + i] */
 } sa_plan;
 
 /* Accepted shapes: D in {64, 128}; block_q in {64, 128}; block_kv = 64; B*H <= 65535;
@@ -112,6 +115,23 @@ sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, 
                                     int block_kv, const int32_t *host_row_ptr,
                                     const int32_t *host_col_idx, void *workspace,
                                     size_t ws_bytes, sa_plan *out, hipStream_t stream);
+
+/* The mask of sparse_attn_plan for queries taken in a per-head order other than their
+ * storage order (head-aware 3-D tiling, Veda page, section 2.2: query blocks that are
+ * compact cubes of the token grid). q stays in storage (raster) order; query position i
+ * of head h is token q_order[h*N + i], so query block I is positions [I*block_q, ...).
+ * k is given already in the order whose consecutive blocks are the KV blocks (for
+ * example moved by sparse_attn_cube_permute). The plan keeps the q_order pointer:
+ * sparse_attn_fwd with this plan reads q through it and writes o (and lse) back to the
+ * storage rows, so o needs no move back. v must be in k's order.
+ * q_order: device int32 [H*N], a permutation of 0..N-1 per head (sparse_attn_cube_order
+ * builds one); it must outlive the plan's use. Entries outside [0, N) are clamped (the
+ * results are then meaningless, but no access leaves the tensors). bf16 only (fp32:
+ * SA_ERR_UNSUPPORTED). Otherwise as sparse_attn_plan. */
+sa_status sparse_attn_plan_ordered(const void *q, const void *k, sa_dtype dtype, int B, int H,
+                                   int N, int D, int block_q, int block_kv, double topk_frac,
+                                   double top_p, const int32_t *q_order, void *workspace,
+                                   size_t ws_bytes, sa_plan *out, hipStream_t stream);
 
 /* Workspace bytes sparse_attn_fwd needs: 0 without the linear branch. */
 size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_linear);
@@ -160,6 +180,12 @@ sa_status sparse_attn_tile_stats(const void *q, const void *k, const float *lse,
 sa_status sparse_attn_cube_permute(const void *src, void *dst, sa_dtype dtype, int B, int H, int N,
                                    int D, int T, int Hg, int W, const int32_t *host_cubes,
                                    int inverse, hipStream_t stream);
+
+/* The same cube orders as an index table for sparse_attn_plan_ordered: for every head h
+ * and position i, order[h*N + pos_h(n)] = n. order: device int32 [H*N]. host_cubes as
+ * for sparse_attn_cube_permute (H <= 128). */
+sa_status sparse_attn_cube_order(int H, int T, int Hg, int W, const int32_t *host_cubes,
+                                 int32_t *order, hipStream_t stream);
 
 /* Diagnostic: y[i] = the router's fp32 exp of x[i] for x[i] <= 0 (0 below -86), evaluated
  * on the device with the router's own code. x, y: device float [n]. */

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 11
+    assert len(decl) == 13
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -183,3 +183,23 @@ def test_cube_permute_validation(lib):
     assert call(cubes=np.array([2, 0, 16, 1, 1, 1])) == E.SA_ERR_INVALID_ARG
     assert call(shape=(1, 2, 21 * 45 * 80, 4)) == E.SA_ERR_UNSUPPORTED   # rows of 8 bytes
     assert call(shape=(1, 129, 21 * 45 * 80, 128), cubes=np.ones(129 * 3)) == E.SA_ERR_UNSUPPORTED
+
+
+def test_plan_ordered_and_cube_order_validation(lib):
+    E = B
+    st = B.SaPlan()
+    shape = (1, 2, 1024, 64, 64, 64)
+    f = lib.sparse_attn_plan_ordered
+    assert f(FAKE, FAKE, 0, *shape, 0.1, 0.9, None, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, *shape, 0.1, 0.9, FAKE, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_UNSUPPORTED
+    assert f(None, FAKE, 0, *shape, 0.1, 0.9, FAKE, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 0, *shape, 1.5, 0.9, FAKE, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+    g = lib.sparse_attn_cube_order
+    c = np.array([1, 4, 16, 2, 2, 2], dtype=np.int32)
+    assert g(2, 4, 16, 16, None, FAKE, None) == E.SA_ERR_INVALID_ARG
+    assert g(2, 4, 16, 16, c.ctypes.data, None, None) == E.SA_ERR_INVALID_ARG
+    assert g(0, 4, 16, 16, c.ctypes.data, FAKE, None) == E.SA_ERR_INVALID_ARG
+    bad = np.array([1, 4, 0, 2, 2, 2], dtype=np.int32)
+    assert g(2, 4, 16, 16, bad.ctypes.data, FAKE, None) == E.SA_ERR_INVALID_ARG
+    big = np.ones(3 * 129, dtype=np.int32)
+    assert g(129, 4, 16, 16, big.ctypes.data, FAKE, None) == E.SA_ERR_UNSUPPORTED

@@ -107,3 +107,48 @@ def test_480p_plan_under_cube_tiling():
                               permute_heads(ent["k32"], w.grid, kc), w.block_q, w.block_kv, w.topk, w.top_p)
     assert np.array_equal(rp, rrp) and np.array_equal(ci, rci)
     log(f"480p cube tiling: nnz {rp[-1]} (tile sparsity {1 - rp[-1] / (w.rows * w.n_kvblk):.4f})")
+
+
+# ------------------------------------------------------------------ query order table
+def test_cube_order_table_bitexact():
+    from oracle import cube_order as oracle_cube_order
+    grid = (5, 12, 20)
+    cubes = [(2, 4, 16), (1, 8, 16), (4, 4, 8)]
+    got = sa.cube_order(3, grid, cubes).cpu().numpy()
+    for h in range(3):
+        assert np.array_equal(got[h], oracle_cube_order(grid, cubes[h]))
+
+
+ORDERED = [
+    # name, H, D, grid, block_q, topk, top_p, linear
+    ("ord_d128", 3, 128, (4, 16, 32), 128, 0.1, 0.9, False),
+    ("ord_d128_ragged_lin", 2, 128, (5, 12, 20), 128, 0.1, 0.85, True),
+    ("ord_d64_q64", 3, 64, (4, 8, 32), 64, 0.05, 0.9, False),
+]
+
+
+@pytest.mark.parametrize("case", ORDERED, ids=[c[0] for c in ORDERED])
+def test_ordered_plan_equals_moved_queries(case):
+    """Gathering q and scattering o through the table is bitwise the same as moving q,
+    running, and moving o back."""
+    name, H, D, grid, bq, topk, p, lin = case
+    w = W.Workload(name, 1, H, D, grid, "bf16", bq, 64, topk, p, 4, linear=lin, seed=3)
+    ent = inputs(w)
+    qc, kc = cubes_for(H, Q_CUBES), cubes_for(H, KV_CUBES)
+    table = sa.cube_order(H, grid, qc)
+    kp = sa.cube_permute(ent["dk"], grid, kc)
+    vp = sa.cube_permute(ent["dv"], grid, kc)
+    qp = sa.cube_permute(ent["dq"], grid, qc)
+    alpha = ent["dalpha"] if lin else None
+    p_ord = sa.plan_ordered(ent["dq"], kp, table, bq, 64, topk, p)
+    p_mov = sa.plan(qp, kp, bq, 64, topk, p)
+    rp1, ci1 = p_ord.csr()
+    rp2, ci2 = p_mov.csr()
+    assert np.array_equal(rp1, rp2) and np.array_equal(ci1, ci2)
+    o1, l1 = sa.fwd(ent["dq"], kp, vp, p_ord, alpha=alpha, return_lse=True)
+    o2, l2 = sa.fwd(qp, kp, vp, p_mov, alpha=alpha, return_lse=True)
+    o2 = sa.cube_permute(o2, grid, qc, inverse=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    l2 = unpermute_heads(l2.cpu().numpy()[..., None], grid, qc)[..., 0]
+    assert np.array_equal(l1.cpu().numpy(), l2)
+    log(f"{name}: ordered path bitwise equal to the moved path (nnz {rp1[-1]})")
