@@ -81,6 +81,21 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
   const int sub = threadIdx.x / kTpb;
   const int lane = threadIdx.x % kTpb;
   const long g = (long)blockIdx.x * kBlocksPerWg + sub;
+  // with a table, this workgroup's row indices are staged in LDS first (one coalesced
+  // load), so the row loads below do not each wait for their own index
+  __shared__ int ordbuf[ORD ? kBlocksPerWg * 128 : 1];
+  if constexpr (ORD) {
+    for (int e = threadIdx.x; e < kBlocksPerWg * bs; e += 256) {
+      const int sb = e / bs, t = e - sb * bs;
+      const long g2 = (long)blockIdx.x * kBlocksPerWg + sb;
+      if (g2 < total_blocks) {
+        const long bh2 = g2 / nblk;
+        const int t2 = (int)(g2 % nblk) * bs + t;
+        if (t2 < N) ordbuf[e] = min(max(order[(size_t)(bh2 % H) * N + t2], 0), N - 1);
+      }
+    }
+    __syncthreads();
+  }
   if (g >= total_blocks) return;
   const long bh = g / nblk;
   const int I = (int)(g % nblk);
@@ -88,16 +103,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
   const int cnt = min(bs, N - t0);
   const T *p = x + ((size_t)bh * N + t0) * D + lane * 8;
   const T *base = x + (size_t)bh * N * D + lane * 8;
-  const int32_t *ord = ORD ? order + (size_t)(bh % H) * N + t0 : nullptr;
+  const int *ord = ORD ? ordbuf + sub * bs : nullptr;
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-#pragma unroll 8
-  for (int t = 0; t < cnt; ++t) {
-    const T *rowp = p + (size_t)t * D;
-    if constexpr (ORD) rowp = base + (size_t)min(max(ord[t], 0), N - 1) * D;
+  // 8 row loads in flight, then their adds in row order (the sum stays sequential)
+  auto row = [&](int t) -> const T * {
+    if constexpr (ORD) return base + (size_t)ord[t] * D;
+    return p + (size_t)t * D;
+  };
+  auto add_row = [&](const T *rp) {
     if constexpr (sizeof(T) == 2) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(rowp);
+      const uint4 w = *reinterpret_cast<const uint4 *>(rp);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -105,12 +122,42 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
         acc[2 * c + 1] = acc[2 * c + 1] + __uint_as_float(ws[c] & 0xffff0000u);
       }
     } else {
-      const float4 a = *reinterpret_cast<const float4 *>(rowp);
-      const float4 b = *reinterpret_cast<const float4 *>(rowp + 4);
+      const float4 a = *reinterpret_cast<const float4 *>(rp);
+      const float4 b = *reinterpret_cast<const float4 *>(rp + 4);
       acc[0] = acc[0] + a.x; acc[1] = acc[1] + a.y; acc[2] = acc[2] + a.z; acc[3] = acc[3] + a.w;
       acc[4] = acc[4] + b.x; acc[5] = acc[5] + b.y; acc[6] = acc[6] + b.z; acc[7] = acc[7] + b.w;
     }
+  };
+  int t = 0;
+  for (; t + 8 <= cnt; t += 8) {
+    if constexpr (sizeof(T) == 2) {
+      uint4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = *reinterpret_cast<const uint4 *>(row(t + u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * c] = acc[2 * c] + __uint_as_float(ws[c] << 16);
+          acc[2 * c + 1] = acc[2 * c + 1] + __uint_as_float(ws[c] & 0xffff0000u);
+        }
+      }
+    } else {
+      float4 a[8], b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a[u] = *reinterpret_cast<const float4 *>(row(t + u));
+        b[u] = *reinterpret_cast<const float4 *>(row(t + u) + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[0] = acc[0] + a[u].x; acc[1] = acc[1] + a[u].y; acc[2] = acc[2] + a[u].z; acc[3] = acc[3] + a[u].w;
+        acc[4] = acc[4] + b[u].x; acc[5] = acc[5] + b[u].y; acc[6] = acc[6] + b[u].z; acc[7] = acc[7] + b[u].w;
+      }
+    }
   }
+  for (; t < cnt; ++t) add_row(row(t));
   const float fc = (float)cnt;
   float *o = out + (size_t)g * D + lane * 8;
   float4 r0 = make_float4(acc[0] / fc, acc[1] / fc, acc[2] / fc, acc[3] / fc);
