@@ -23,6 +23,8 @@ Two tracks:
   mean attention mass per tile, in float64.
 * ``oracle.tiling``: the group-major token order of head-aware 3-D tiling (Veda page,
   section 2.2: a per-head factorisation of the tile into a spatio-temporal cube).
+* ``oracle.backward``: the gradients dQ, dK, dV of block-sparse attention in float64
+  (the pages fine-tune through the sparse kernel).
 
 Parity pins (tests marked "not gpu") tie both tracks to facts outside the oracle:
 closed forms, library routines, brute force and hand-derived fixtures. Parity of the
@@ -35,11 +37,12 @@ from .attention import (sparse_attention, dense_attention, brute_masked_attentio
                         linear_branch, blend, phi, dense_plan, csr_to_mask)
 from .heatmap import tile_heatmap
 from .tiling import cube_order, permute_heads, unpermute_heads
+from .backward import sparse_attention_backward
 
 __all__ = [
     "exp_sa", "pool_blocks", "block_scores", "tree_sum", "select_row", "topk_count",
     "oracle_plan", "plan_stats", "score_scale",
     "sparse_attention", "dense_attention", "brute_masked_attention", "linear_branch",
     "blend", "phi", "dense_plan", "csr_to_mask", "tile_heatmap", "cube_order", "permute_heads",
-    "unpermute_heads",
+    "unpermute_heads", "sparse_attention_backward",
 ]
