@@ -6,6 +6,7 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
     fwd(q, k, v, plan, alpha=None)              attention over the kept tiles, with the
                                                 optional elu+1 linear branch blend
     plan_dense(q, ...), plan_from_csr(q, ...)   all-ones and caller-given masks
+    bwd(q, k, v, o, lse, dout, plan)            gradients dq, dk, dv over the same mask
     tile_stats(q, k, lse, ...)                  ground-truth tile heatmap (max and mean
                                                 mass of full attention per tile)
     cube_permute(x, grid, cubes, inverse)       head-aware 3-D tiling: raster <-> per-head
@@ -17,13 +18,13 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
 All computation happens in the library's HIP kernels; torch supplies device memory and
 streams.
 """
-from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, cube_order,
+from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, bwd, cube_order,
                        cube_permute, fwd, load_library, plan_ordered,
                        plan, plan_dense, plan_from_csr, plan_workspace_bytes, router_exp, tile_stats,
                        version)
 
 __all__ = [
-    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "cube_order",
+    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "bwd", "cube_order",
     "cube_permute", "fwd", "load_library", "plan_ordered",
     "plan", "plan_dense", "plan_from_csr", "plan_workspace_bytes", "router_exp", "tile_stats",
     "version",

@@ -24,6 +24,7 @@ SA_BF16, SA_FP32 = 0, 1
 EXPORTS = (
     "sparse_attn_plan_workspace_bytes", "sparse_attn_plan", "sparse_attn_plan_dense",
     "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
+    "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd",
     "sparse_attn_plan_ordered", "sparse_attn_tile_stats", "sparse_attn_cube_permute",
     "sparse_attn_cube_order", "sparse_attn_router_exp", "sparse_attn_status_string",
     "sparse_attn_version",
@@ -81,6 +82,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_cube_permute.restype = i32
     lib.sparse_attn_cube_order.argtypes = [i32] * 4 + [vp, vp, vp]
     lib.sparse_attn_cube_order.restype = i32
+    lib.sparse_attn_bwd_workspace_bytes.argtypes = [i32] * 6
+    lib.sparse_attn_bwd_workspace_bytes.restype = sz
+    lib.sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp,
+                                    vp, sz, vp]
+    lib.sparse_attn_bwd.restype = i32
     lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
     lib.sparse_attn_router_exp.restype = i32
     lib.sparse_attn_status_string.argtypes = [i32]
@@ -310,6 +316,29 @@ def fwd(q, k, v, plan: Plan, alpha=None, return_lse: bool = False, out=None, lse
                                ws.numel() if ws is not None else 0, _stream(stream)),
            "sparse_attn_fwd")
     return (o, lse) if return_lse else o
+
+
+def bwd(q, k, v, o, lse, dout, plan: Plan, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of fwd(q, k, v, plan) for the upstream gradient dout, from
+    the forward's o and lse (see sparse_attn_bwd)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    _check_qkv(q, o, dout)
+    B, H, N, D = q.shape
+    if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+            and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] GPU tensor")
+    need = lib.sparse_attn_bwd_workspace_bytes(B, H, N, D, plan.st.block_q, plan.st.block_kv)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "bwd shape")
+    ws = workspace if workspace is not None else _new_ws(need, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.sparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               dout.data_ptr(), _dtype_code(q), B, H, N, D, ctypes.byref(plan.st),
+                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                               _stream(stream)), "sparse_attn_bwd")
+    return dq, dk, dv
 
 
 def tile_stats(q, k, lse, block_q: int = 128, block_kv: int = 64, stream=None):

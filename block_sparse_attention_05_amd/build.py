@@ -31,6 +31,7 @@ SOURCES = {
     "linear.hip": [],
     "heatmap.hip": [],
     "tiling.hip": [],
+    "backward.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

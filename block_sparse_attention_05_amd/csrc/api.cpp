@@ -320,6 +320,87 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   return hip_status(launch_fwd(a, dtype, stream));
 }
 
+namespace {
+struct BwdLayout {
+  size_t dvec, tbits, ccount, col_ptr, row_idx, total;
+  int nwq;
+};
+BwdLayout bwd_layout(const Shape &s) {
+  BwdLayout L{};
+  const size_t BH = (size_t)s.B * s.H;
+  const size_t C = BH * s.nKV;
+  L.nwq = ceil_div(s.nQ, 32);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.dvec = take(BH * (size_t)s.N * 4);
+  L.tbits = take(C * L.nwq * 4);
+  L.ccount = take(C * 4);
+  L.col_ptr = take((C + 1) * 4);
+  L.row_idx = take((size_t)s.R * s.nKV * 4);
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t sparse_attn_bwd_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv) {
+  Shape s;
+  if (check_shape(B, H, N, D, block_q, block_kv, &s) != SA_OK) return 0;
+  return bwd_layout(s).total;
+}
+
+sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                          const float *lse, const void *dout, sa_dtype dtype, int B, int H,
+                          int N, int D, const sa_plan *plan, void *dq, void *dk, void *dv,
+                          void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !plan || !dq || !dk || !dv) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, plan->block_q, plan->block_kv, &s);
+  if (st != SA_OK) return st;
+  if (plan->B != B || plan->H != H || plan->N != N || plan->D != D || plan->dtype != (int)dtype ||
+      plan->row_ptr == nullptr || plan->col_idx == nullptr)
+    return SA_ERR_PLAN_MISMATCH;
+  if (dtype != SA_BF16 || plan->q_order != nullptr) return SA_ERR_UNSUPPORTED;
+  const BwdLayout L = bwd_layout(s);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != SA_OK) return st;
+  char *ws = static_cast<char *>(workspace);
+  BwdArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.o = (const uint16_t *)o;
+  a.dout = (const uint16_t *)dout;
+  a.lse = lse;
+  a.dvec = reinterpret_cast<float *>(ws + L.dvec);
+  a.dq = (uint16_t *)dq;
+  a.dk = (uint16_t *)dk;
+  a.dv = (uint16_t *)dv;
+  a.row_ptr = plan->row_ptr;
+  a.col_idx = plan->col_idx;
+  a.row_order = plan->row_order;
+  a.col_ptr = reinterpret_cast<int32_t *>(ws + L.col_ptr);
+  a.row_idx = reinterpret_cast<int32_t *>(ws + L.row_idx);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.block_q = s.bq;
+  a.n_qblk = s.nQ;
+  a.n_kvblk = s.nKV;
+  a.scale = (float)(1.0 / sqrt((double)D));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  BwdBufs w;
+  w.tbits = reinterpret_cast<uint32_t *>(ws + L.tbits);
+  w.nwq = L.nwq;
+  w.ccount = reinterpret_cast<int32_t *>(ws + L.ccount);
+  return hip_status(launch_bwd(a, w, stream));
+}
+
 sa_status sparse_attn_tile_stats(const void *q, const void *k, const float *lse, sa_dtype dtype,
                                  int B, int H, int N, int D, int block_q, int block_kv,
                                  float *tile_max, float *tile_mass, hipStream_t stream) {

@@ -71,6 +71,24 @@ hipError_t launch_cube_permute(const void *src, void *dst, int BH, int H, int N,
                                int Hg, int W, const CubeTable &cubes, int inverse, hipStream_t s);
 hipError_t launch_cube_order(int H, int T, int Hg, int W, const CubeTable &cubes, int32_t *order,
                              hipStream_t s);
+// Backward (backward.hip).
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *o, *dout;   // [B, H, N, D] bf16
+  const float *lse;                        // [B, H, N] from the forward
+  float *dvec;                             // [B, H, N] workspace: rowsum(dO * O)
+  uint16_t *dq, *dk, *dv;                  // [B, H, N, D] bf16
+  const int32_t *row_ptr, *col_idx, *row_order;
+  int32_t *col_ptr, *row_idx;              // CSC of the mask (workspace)
+  int B, H, N, D, block_q, n_qblk, n_kvblk;
+  float scale;                             // 1/sqrt(D)
+  float scale_log2;                        // log2(e)/sqrt(D)
+};
+struct BwdBufs {
+  uint32_t *tbits;   // [B*H*n_kvblk, nwq] column-major bitmap of the mask
+  int nwq;           // ceil(n_qblk / 32)
+  int32_t *ccount;   // [B*H*n_kvblk]
+};
+hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s);
 // Tile heatmap, pass 2 (heatmap.hip): per (row, KV block) max and mean mass of exp(s - lse).
 hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
                              int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s);

@@ -150,6 +150,23 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
                           const float *alpha, void *o, float *lse,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes sparse_attn_bwd needs for this shape. */
+size_t sparse_attn_bwd_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv);
+
+/* Gradients of block-sparse attention over the plan's kept tiles (the pages fine-tune
+ * through the sparse kernel: SpargeAttention2 page, section 2; SLA2 page). With
+ * c = 1/sqrt(D), P = exp(c*q k^T - lse) on kept tiles and Dv = rowsum(dO * o):
+ *   dq = c * (P * (dO v^T - Dv)) k,  dk = c * (P * (dO v^T - Dv))^T q,  dv = P^T dO.
+ * q, k, v, o, dout: device [B, H, N, D] bf16 (o and lse as sparse_attn_fwd wrote them
+ * with this plan, without the linear branch); lse: device float [B, H, N].
+ * dq, dk, dv: device [B, H, N, D] bf16, written in full (zeros where nothing is kept).
+ * Deterministic (no atomics on values). bf16 only and plans without a query order;
+ * otherwise SA_ERR_UNSUPPORTED. workspace: sparse_attn_bwd_workspace_bytes bytes. */
+sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                          const float *lse, const void *dout, sa_dtype dtype, int B, int H,
+                          int N, int D, const sa_plan *plan, void *dq, void *dk, void *dv,
+                          void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Ground-truth tile heatmap of full attention (Veda page, section 2.1: the reference mask
  * max-pools the full attention matrix over query x key tiles; section 2.3: two passes).
  * Pass 1 is sparse_attn_fwd on a sparse_attn_plan_dense plan with an lse output; this

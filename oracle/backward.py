@@ -32,11 +32,20 @@ def _row_tokens(blocks: np.ndarray, block_kv: int, N: int) -> np.ndarray:
     return t[t < N]
 
 
-def sparse_attention_backward(q, k, v, do, row_ptr, col_idx, block_q: int,
-                              block_kv: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+def sparse_attention_backward(q, k, v, do, row_ptr, col_idx, block_q: int, block_kv: int,
+                              rows=None, o=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """(dQ, dK, dV), each [B, H, N, D] float64, for O = block-sparse attention of q, k, v
-    [B, H, N, D] under the CSR mask, and the upstream gradient do [B, H, N, D]."""
+    [B, H, N, D] under the CSR mask, and the upstream gradient do [B, H, N, D].
+
+    With ``rows`` (row indices r = (b*H + h)*nQ + I), only those query blocks contribute:
+    dQ is then complete on those blocks, and dK, dV on every KV block all of whose
+    keeping rows are included.
+
+    With ``o`` (the forward output as a caller stored it, for example rounded to bf16),
+    Dv is formed from that o instead of the exact one, as a backward that reuses the
+    forward's output does."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    o_given = None if o is None else np.asarray(o, dtype=np.float64)
     B, H, N, D = q.shape
     nQ = -(-N // block_q)
     c = 1.0 / math.sqrt(D)
@@ -45,25 +54,25 @@ def sparse_attention_backward(q, k, v, do, row_ptr, col_idx, block_q: int,
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for b in range(B):
-        for h in range(H):
-            for I in range(nQ):
-                r = (b * H + h) * nQ + I
-                tok = _row_tokens(col_idx[row_ptr[r]:row_ptr[r + 1]], block_kv, N)
-                if tok.size == 0:
-                    continue
-                qs = slice(I * block_q, min(N, (I + 1) * block_q))
-                qi, gi = q[b, h, qs], do[b, h, qs]
-                kj, vj = k[b, h, tok], v[b, h, tok]
-                s = c * (qi @ kj.T)
-                s -= s.max(axis=1, keepdims=True)
-                p = np.exp(s)
-                p /= p.sum(axis=1, keepdims=True)
-                o = p @ vj
-                dp = gi @ vj.T
-                dvec = (gi * o).sum(axis=1, keepdims=True)
-                ds = p * (dp - dvec)
-                dq[b, h, qs] = c * (ds @ kj)
-                dk[b, h, tok] += c * (ds.T @ qi)
-                dv[b, h, tok] += p.T @ gi
+    todo = range(B * H * nQ) if rows is None else sorted(set(int(r) for r in rows))
+    for r in todo:
+        bh, I = divmod(r, nQ)
+        b, h = divmod(bh, H)
+        tok = _row_tokens(col_idx[row_ptr[r]:row_ptr[r + 1]], block_kv, N)
+        if tok.size == 0:
+            continue
+        qs = slice(I * block_q, min(N, (I + 1) * block_q))
+        qi, gi = q[b, h, qs], do[b, h, qs]
+        kj, vj = k[b, h, tok], v[b, h, tok]
+        s = c * (qi @ kj.T)
+        s -= s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        oi = p @ vj if o_given is None else o_given[b, h, qs]
+        dp = gi @ vj.T
+        dvec = (gi * oi).sum(axis=1, keepdims=True)
+        ds = p * (dp - dvec)
+        dq[b, h, qs] = c * (ds @ kj)
+        dk[b, h, tok] += c * (ds.T @ qi)
+        dv[b, h, tok] += p.T @ gi
     return dq, dk, dv

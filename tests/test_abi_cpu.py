@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 13
+    assert len(decl) == 15
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -203,3 +203,31 @@ def test_plan_ordered_and_cube_order_validation(lib):
     assert g(2, 4, 16, 16, bad.ctypes.data, FAKE, None) == E.SA_ERR_INVALID_ARG
     big = np.ones(3 * 129, dtype=np.int32)
     assert g(129, 4, 16, 16, big.ctypes.data, FAKE, None) == E.SA_ERR_UNSUPPORTED
+
+
+def test_bwd_validation(lib):
+    E = B
+    st = B.SaPlan()
+    st.B, st.H, st.N, st.D, st.block_q, st.block_kv = 1, 2, 1024, 64, 64, 64
+    st.n_qblk, st.n_kvblk, st.dtype = 16, 16, 0
+    st.row_ptr, st.col_idx, st.row_order = FAKE, FAKE, FAKE
+    f = lib.sparse_attn_bwd
+    good = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dt=0, shape=(1, 2, 1024, 64),
+                dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dt"], *a["shape"],
+                 ctypes.byref(st), a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert call(**{name: None}) == E.SA_ERR_INVALID_ARG, name
+    assert call(shape=(1, 2, 2048, 64)) == E.SA_ERR_PLAN_MISMATCH
+    assert call(dt=1) == E.SA_ERR_PLAN_MISMATCH            # the plan was made for bf16
+    assert call(wsb=16) == E.SA_ERR_WORKSPACE
+    assert call(ws=None) == E.SA_ERR_WORKSPACE
+    need = lib.sparse_attn_bwd_workspace_bytes(1, 2, 1024, 64, 64, 64)
+    assert need > 0 and lib.sparse_attn_bwd_workspace_bytes(1, 2, 1024, 80, 64, 64) == 0
+    st.q_order = FAKE
+    assert call() == E.SA_ERR_UNSUPPORTED                   # ordered plans
+    st.q_order = None

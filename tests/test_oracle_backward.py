@@ -68,3 +68,17 @@ def test_unkept_tokens_get_no_gradient_and_empty_rows_no_dq():
     assert dk[0, 0, 32:40].any() and dv[0, 0, 0:16].any()
     assert not dq[0, 0, 16:32].any()
     assert dq[0, 0, 0:16].any() and dq[0, 0, 32:40].any()
+
+
+def test_given_output_changes_only_dv_term():
+    """With o given as the exact output, the result is unchanged; with o perturbed, dV is
+    unchanged (it does not use Dv) while dQ and dK move."""
+    q, k, v, g, rp, ci = _case(seed=5)
+    ref = sparse_attention_backward(q, k, v, g, rp, ci, 16, 16)
+    o = sparse_attention(q, k, v, rp, ci, 16, 16)
+    same = sparse_attention_backward(q, k, v, g, rp, ci, 16, 16, o=o)
+    for a, b in zip(ref, same):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    moved = sparse_attention_backward(q, k, v, g, rp, ci, 16, 16, o=o * 1.01)
+    np.testing.assert_array_equal(moved[2], ref[2])
+    assert not np.allclose(moved[0], ref[0])
