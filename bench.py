@@ -154,6 +154,41 @@ def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 20.0):
     }
 
 
+def time_backward(sa, torch, w, dq, dk, dv, p, pairs, args, stream):
+    """Times sparse_attn_bwd over the plan p. Algorithmic work per kept (query, key) pair:
+    the recomputed scores, dP = dO V^T, dV, dK and dQ, 2*D flops each (10*D); the kernels
+    form S and dP once per direction (14*D actually issued)."""
+    rng = np.random.default_rng([7, w.B, w.H, w.N, w.D])
+    ddo = torch.from_numpy(W.f64_to_bf16_bits(rng.normal(size=(w.B, w.H, w.N, w.D))).view(np.int16)
+                           ).view(torch.bfloat16).cuda()
+    o, lse = sa.fwd(dq, dk, dv, p, return_lse=True)
+    ws = torch.empty(sa.bwd_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv),
+                     dtype=torch.uint8, device="cuda")
+    grads = tuple(torch.empty_like(dq) for _ in range(3))
+    for _ in range(max(1, args.warmup)):
+        sa.bwd(dq, dk, dv, o, lse, ddo, p, workspace=ws, out=grads)
+    n = max(3, args.steps)
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        e0[i].record(stream)
+        sa.bwd(dq, dk, dv, o, lse, ddo, p, workspace=ws, out=grads)
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in zip(e0, e1)]
+    t = float(np.mean(ms))
+    log(f"backward {t:.3f} ms (median {float(np.median(ms)):.3f})")
+    return {
+        "ms_bwd": round(t, 4),
+        "ms_bwd_median": round(float(np.median(ms)), 4),
+        "ms_bwd_min": round(float(np.min(ms)), 4),
+        "bwd_tflops_alg": round(10.0 * w.D * pairs / t / 1e9, 2),
+        "bwd_tflops_issued": round(14.0 * w.D * pairs / t / 1e9, 2),
+        "flops_per_pair": "10*D algorithmic (S, dP, dV, dK, dQ); 14*D issued",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +204,9 @@ def main():
     ap.add_argument("--quality", action="store_true",
                     help="also build the ground-truth tile heatmap of full attention (two "
                          "passes) and report the router mask's recall and retained mass")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward (dq, dk, dv) over the step's plan, from the "
+                         "forward's o and lse and a synthetic upstream gradient")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -337,6 +375,10 @@ def main():
             "kernel": "sparse_fwd_bf16_kernel" if w.dtype == "bf16" else "sparse_fwd_kernel",
         },
     }
+    if args.backward:
+        if w.dtype != "bf16" or q_table is not None:
+            raise SystemExit("--backward needs a bf16 workload in raster order (no --cubes)")
+        out["backward"] = time_backward(sa, torch, w, dq, dk, dv, p, pairs, args, stream)
     if args.copy_probe_mib > 0:
         # a plain copy of known size: HBM counters of this kernel calibrate the others
         nb = args.copy_probe_mib << 20

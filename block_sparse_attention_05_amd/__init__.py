@@ -18,13 +18,13 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
 All computation happens in the library's HIP kernels; torch supplies device memory and
 streams.
 """
-from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, bwd, cube_order,
-                       cube_permute, fwd, load_library, plan_ordered,
+from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, bwd, bwd_workspace_bytes,
+                       cube_order, cube_permute, fwd, load_library, plan_ordered,
                        plan, plan_dense, plan_from_csr, plan_workspace_bytes, router_exp, tile_stats,
                        version)
 
 __all__ = [
-    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "bwd", "cube_order",
+    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "bwd", "bwd_workspace_bytes", "cube_order",
     "cube_permute", "fwd", "load_library", "plan_ordered",
     "plan", "plan_dense", "plan_from_csr", "plan_workspace_bytes", "router_exp", "tile_stats",
     "version",

@@ -198,6 +198,10 @@ def plan_workspace_bytes(B, H, N, D, block_q, block_kv) -> int:
     return int(load_library().sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv))
 
 
+def bwd_workspace_bytes(B, H, N, D, block_q, block_kv) -> int:
+    return int(load_library().sparse_attn_bwd_workspace_bytes(B, H, N, D, block_q, block_kv))
+
+
 def plan(q, k, block_q: int = 128, block_kv: int = 64, topk: float = 0.05, top_p: float = 0.9,
          stream=None, workspace=None) -> Plan:
     """The hybrid top-k / top-p block mask of q, k [B, H, N, D] (see sparse_attn_plan)."""
@@ -318,9 +322,10 @@ def fwd(q, k, v, plan: Plan, alpha=None, return_lse: bool = False, out=None, lse
     return (o, lse) if return_lse else o
 
 
-def bwd(q, k, v, o, lse, dout, plan: Plan, workspace=None, stream=None):
+def bwd(q, k, v, o, lse, dout, plan: Plan, workspace=None, out=None, stream=None):
     """Gradients (dq, dk, dv) of fwd(q, k, v, plan) for the upstream gradient dout, from
-    the forward's o and lse (see sparse_attn_bwd)."""
+    the forward's o and lse (see sparse_attn_bwd). ``out`` = (dq, dk, dv) tensors shaped
+    like q to write into."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -333,7 +338,13 @@ def bwd(q, k, v, o, lse, dout, plan: Plan, workspace=None, stream=None):
     if need == 0:
         raise SparseAttnError(SA_ERR_UNSUPPORTED, "bwd shape")
     ws = workspace if workspace is not None else _new_ws(need, q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _check_qkv(dq, dk, dv)
+        if dq.shape != q.shape or dq.dtype != q.dtype:
+            raise ValueError("out tensors must match q's shape and dtype")
     _check(lib.sparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                dout.data_ptr(), _dtype_code(q), B, H, N, D, ctypes.byref(plan.st),
                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
