@@ -25,6 +25,9 @@ Two tracks:
   section 2.2: a per-head factorisation of the tile into a spatio-temporal cube).
 * ``oracle.backward``: the gradients dQ, dK, dV of block-sparse attention in float64
   (the pages fine-tune through the sparse kernel).
+* ``oracle.fp8``: the low-bit forward (SLA2 page, quantisation-aware fine-tuning):
+  Q, K, V quantised to OCP FP8 E4M3 with power-of-two group scales, then attention in
+  float64 on the decoded values.
 
 Parity pins (tests marked "not gpu") tie both tracks to facts outside the oracle:
 closed forms, library routines, brute force and hand-derived fixtures. Parity of the
@@ -38,11 +41,14 @@ from .attention import (sparse_attention, dense_attention, brute_masked_attentio
 from .heatmap import tile_heatmap
 from .tiling import cube_order, permute_heads, unpermute_heads
 from .backward import sparse_attention_backward
+from .fp8 import (e4m3_decode, e4m3_encode, scale_exponent, quantize_qkv, dequantize,
+                  fp8_attention)
 
 __all__ = [
     "exp_sa", "pool_blocks", "block_scores", "tree_sum", "select_row", "topk_count",
     "oracle_plan", "plan_stats", "score_scale",
     "sparse_attention", "dense_attention", "brute_masked_attention", "linear_branch",
     "blend", "phi", "dense_plan", "csr_to_mask", "tile_heatmap", "cube_order", "permute_heads",
-    "unpermute_heads", "sparse_attention_backward",
+    "unpermute_heads", "sparse_attention_backward", "e4m3_decode", "e4m3_encode",
+    "scale_exponent", "quantize_qkv", "dequantize", "fp8_attention",
 ]
