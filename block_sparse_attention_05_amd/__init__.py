@@ -7,6 +7,9 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
                                                 optional elu+1 linear branch blend
     plan_dense(q, ...), plan_from_csr(q, ...)   all-ones and caller-given masks
     bwd(q, k, v, o, lse, dout, plan)            gradients dq, dk, dv over the same mask
+    quantize_fp8(q, k, v, block_q), fwd_fp8     the low-bit forward: FP8 E4M3 codes with
+                                                power-of-two group scales, then attention
+                                                on fp8 MFMA
     tile_stats(q, k, lse, ...)                  ground-truth tile heatmap (max and mean
                                                 mass of full attention per tile)
     cube_permute(x, grid, cubes, inverse)       head-aware 3-D tiling: raster <-> per-head
@@ -18,13 +21,13 @@ Thin Python face of libsparse_attn.so (C ABI in include/sparse_attn.h):
 All computation happens in the library's HIP kernels; torch supplies device memory and
 streams.
 """
-from ._binding import (EXPORTS, SA_BF16, SA_FP32, Plan, SaPlan, SparseAttnError, bwd, bwd_workspace_bytes,
-                       cube_order, cube_permute, fwd, load_library, plan_ordered,
+from ._binding import (EXPORTS, SA_BF16, SA_FP32, Fp8Pack, Plan, SaPlan, SparseAttnError, bwd,
+                       bwd_workspace_bytes, cube_order, cube_permute, fp8_pack_bytes, fwd_fp8, quantize_fp8, fwd, load_library, plan_ordered,
                        plan, plan_dense, plan_from_csr, plan_workspace_bytes, router_exp, tile_stats,
                        version)
 
 __all__ = [
-    "EXPORTS", "SA_BF16", "SA_FP32", "Plan", "SaPlan", "SparseAttnError", "bwd", "bwd_workspace_bytes", "cube_order",
+    "EXPORTS", "SA_BF16", "SA_FP32", "Fp8Pack", "fp8_pack_bytes", "fwd_fp8", "quantize_fp8", "Plan", "SaPlan", "SparseAttnError", "bwd", "bwd_workspace_bytes", "cube_order",
     "cube_permute", "fwd", "load_library", "plan_ordered",
     "plan", "plan_dense", "plan_from_csr", "plan_workspace_bytes", "router_exp", "tile_stats",
     "version",

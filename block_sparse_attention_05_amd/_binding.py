@@ -26,7 +26,8 @@ EXPORTS = (
     "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd",
     "sparse_attn_plan_ordered", "sparse_attn_tile_stats", "sparse_attn_cube_permute",
-    "sparse_attn_cube_order", "sparse_attn_router_exp", "sparse_attn_status_string",
+    "sparse_attn_cube_order", "sparse_attn_fp8_pack_bytes", "sparse_attn_quantize_fp8",
+    "sparse_attn_fwd_fp8", "sparse_attn_router_exp", "sparse_attn_status_string",
     "sparse_attn_version",
 )
 
@@ -87,6 +88,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp,
                                     vp, sz, vp]
     lib.sparse_attn_bwd.restype = i32
+    lib.sparse_attn_fp8_pack_bytes.argtypes = [i32] * 6
+    lib.sparse_attn_fp8_pack_bytes.restype = sz
+    lib.sparse_attn_quantize_fp8.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [vp, sz, vp]
+    lib.sparse_attn_quantize_fp8.restype = i32
+    lib.sparse_attn_fwd_fp8.argtypes = [vp, sz, i32, i32, i32, i32, pplan, vp, vp, vp]
+    lib.sparse_attn_fwd_fp8.restype = i32
     lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
     lib.sparse_attn_router_exp.restype = i32
     lib.sparse_attn_status_string.argtypes = [i32]
@@ -350,6 +357,83 @@ def bwd(q, k, v, o, lse, dout, plan: Plan, workspace=None, out=None, stream=None
                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
                                _stream(stream)), "sparse_attn_bwd")
     return dq, dk, dv
+
+
+class Fp8Pack:
+    """FP8 E4M3 codes and group exponents of q, k, v in one device buffer (layout as
+    documented for sparse_attn_fp8_pack_bytes)."""
+
+    def __init__(self, buf, shape, block_q: int, block_kv: int):
+        self.buf = buf
+        self.shape = tuple(shape)
+        self.block_q = block_q
+        self.block_kv = block_kv
+
+    def _parts(self):
+        B, H, N, D = self.shape
+        BH = B * H
+        nQ, nKV = -(-N // self.block_q), -(-N // 64)
+        sizes = [("q8", BH * N * D), ("k8", BH * N * D), ("vt8", BH * nKV * D * 64),
+                 ("qe", BH * nQ * 4), ("ke", BH * nKV * 4), ("ve", BH * D * 4), ("vamax", BH * D * 4)]
+        off, out = 0, {}
+        for name, n in sizes:
+            out[name] = (off, n)
+            off = (off + n + 255) & ~255
+        return out
+
+    def part(self, name: str):
+        """A torch view of one part: uint8 codes or int32 exponents."""
+        torch = _torch()
+        off, n = self._parts()[name]
+        B, H, N, D = self.shape
+        nQ, nKV = -(-N // self.block_q), -(-N // 64)
+        raw = self.buf[off:off + n]
+        shapes = {"q8": (B, H, N, D), "k8": (B, H, N, D), "vt8": (B, H, nKV, D, 64),
+                  "qe": (B, H, nQ), "ke": (B, H, nKV), "ve": (B, H, D), "vamax": (B, H, D)}
+        t = raw if name in ("q8", "k8", "vt8") else raw.view(torch.int32)
+        return t.view(shapes[name])
+
+
+def fp8_pack_bytes(B, H, N, D, block_q=128, block_kv=64) -> int:
+    return int(load_library().sparse_attn_fp8_pack_bytes(B, H, N, D, block_q, block_kv))
+
+
+def quantize_fp8(q, k, v, block_q: int = 128, block_kv: int = 64, out: Optional[Fp8Pack] = None,
+                 stream=None) -> Fp8Pack:
+    """Quantises bf16 q, k, v [B, H, N, D] to an FP8 pack (see sparse_attn_quantize_fp8)."""
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    need = lib.sparse_attn_fp8_pack_bytes(B, H, N, D, block_q, block_kv)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "fp8 pack shape")
+    pack = out if out is not None else Fp8Pack(_new_ws(need, q.device), q.shape, block_q, block_kv)
+    if pack.shape != tuple(q.shape) or pack.block_q != block_q:
+        raise ValueError("pack was made for another shape or block_q")
+    _check(lib.sparse_attn_quantize_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, N, D,
+                                        block_q, block_kv, pack.buf.data_ptr(), pack.buf.numel(),
+                                        _stream(stream)), "sparse_attn_quantize_fp8")
+    return pack
+
+
+def fwd_fp8(pack: Fp8Pack, plan: Plan, return_lse: bool = False, out=None, lse=None, stream=None):
+    """Block-sparse attention over the plan's kept tiles from an FP8 pack (see
+    sparse_attn_fwd_fp8). Returns o (bf16 [B, H, N, D]) and, with return_lse, lse."""
+    torch = _torch()
+    lib = load_library()
+    B, H, N, D = pack.shape
+    if plan.shape != pack.shape or plan.st.block_q != pack.block_q:
+        raise ValueError("plan and pack disagree on shape or block_q")
+    dev = pack.buf.device
+    o = out if out is not None else torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    if o.shape != (B, H, N, D) or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("o must be a contiguous bf16 [B, H, N, D] tensor")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(lib.sparse_attn_fwd_fp8(pack.buf.data_ptr(), pack.buf.numel(), B, H, N, D, ctypes.byref(plan.st),
+                                   o.data_ptr(), lse.data_ptr() if return_lse else None, _stream(stream)),
+           "sparse_attn_fwd_fp8")
+    return (o, lse) if return_lse else o
 
 
 def tile_stats(q, k, lse, block_q: int = 128, block_kv: int = 64, stream=None):

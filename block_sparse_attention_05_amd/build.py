@@ -32,6 +32,7 @@ SOURCES = {
     "heatmap.hip": [],
     "tiling.hip": [],
     "backward.hip": [],
+    "fp8.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

@@ -321,6 +321,96 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
 }
 
 namespace {
+struct Fp8Layout {
+  size_t q8, k8, vt8, qe, ke, ve, vamax, total;
+};
+Fp8Layout fp8_layout(const Shape &s) {
+  Fp8Layout L{};
+  const size_t BH = (size_t)s.B * s.H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.q8 = take(BH * s.N * s.D);
+  L.k8 = take(BH * s.N * s.D);
+  L.vt8 = take(BH * s.nKV * s.D * 64);
+  L.qe = take(BH * s.nQ * 4);
+  L.ke = take(BH * s.nKV * 4);
+  L.ve = take(BH * s.D * 4);
+  L.vamax = take(BH * s.D * 4);
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t sparse_attn_fp8_pack_bytes(int B, int H, int N, int D, int block_q, int block_kv) {
+  Shape s;
+  if (check_shape(B, H, N, D, block_q, block_kv, &s) != SA_OK) return 0;
+  return fp8_layout(s).total;
+}
+
+sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, sa_dtype dtype, int B, int H,
+                                   int N, int D, int block_q, int block_kv, void *pack, size_t pack_bytes,
+                                   hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
+  if (st != SA_OK) return st;
+  if (dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  const Fp8Layout L = fp8_layout(s);
+  st = check_ws(pack, pack_bytes, L.total);
+  if (st != SA_OK) return st;
+  char *pk = static_cast<char *>(pack);
+  Fp8Pack p{reinterpret_cast<uint8_t *>(pk + L.q8),   reinterpret_cast<uint8_t *>(pk + L.k8),
+            reinterpret_cast<uint8_t *>(pk + L.vt8),  reinterpret_cast<int32_t *>(pk + L.qe),
+            reinterpret_cast<int32_t *>(pk + L.ke),   reinterpret_cast<int32_t *>(pk + L.ve),
+            reinterpret_cast<uint32_t *>(pk + L.vamax)};
+  return hip_status(launch_quantize_fp8(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                        static_cast<const uint16_t *>(v), B * H, N, D, s.bq, p, stream));
+}
+
+sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H, int N, int D,
+                              const sa_plan *plan, void *o, float *lse, hipStream_t stream) {
+  if (pack == nullptr || plan == nullptr || o == nullptr) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, plan->block_q, plan->block_kv, &s);
+  if (st != SA_OK) return st;
+  if (plan->B != B || plan->H != H || plan->N != N || plan->D != D || plan->n_qblk != s.nQ ||
+      plan->n_kvblk != s.nKV)
+    return SA_ERR_PLAN_MISMATCH;
+  if (plan->row_ptr == nullptr || plan->col_idx == nullptr) return SA_ERR_INVALID_ARG;
+  if (plan->dtype != SA_BF16 || plan->q_order != nullptr) return SA_ERR_UNSUPPORTED;
+  const Fp8Layout L = fp8_layout(s);
+  st = check_ws(pack, pack_bytes, L.total);
+  if (st != SA_OK) return st;
+  const char *pk = static_cast<const char *>(pack);
+  Fp8FwdArgs a{};
+  a.q8 = reinterpret_cast<const uint8_t *>(pk + L.q8);
+  a.k8 = reinterpret_cast<const uint8_t *>(pk + L.k8);
+  a.vt8 = reinterpret_cast<const uint8_t *>(pk + L.vt8);
+  a.qe = reinterpret_cast<const int32_t *>(pk + L.qe);
+  a.ke = reinterpret_cast<const int32_t *>(pk + L.ke);
+  a.ve = reinterpret_cast<const int32_t *>(pk + L.ve);
+  a.o = static_cast<uint16_t *>(o);
+  a.lse = lse;
+  a.row_ptr = plan->row_ptr;
+  a.col_idx = plan->col_idx;
+  a.row_order = plan->row_order;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.block_q = s.bq;
+  a.n_qblk = s.nQ;
+  a.n_kvblk = s.nKV;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  return hip_status(launch_fwd_fp8(a, stream));
+}
+
+namespace {
 struct BwdLayout {
   size_t dvec, tbits, ccount, col_ptr, row_idx, total;
   int nwq;

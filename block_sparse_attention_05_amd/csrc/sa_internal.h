@@ -89,6 +89,24 @@ struct BwdBufs {
   int32_t *ccount;   // [B*H*n_kvblk]
 };
 hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s);
+// Low-bit forward (fp8.hip): OCP FP8 E4M3 codes with power-of-two group exponents.
+struct Fp8Pack {
+  uint8_t *q8, *k8, *vt8;   // [B,H,N,D], [B,H,N,D], [B,H,nKV,D,64]
+  int32_t *qe, *ke, *ve;    // [B,H,nQ], [B,H,nKV], [B,H,D]
+  uint32_t *vamax;          // [B,H,D] scratch
+};
+hipError_t launch_quantize_fp8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int BH, int N, int D,
+                               int bq, const Fp8Pack &p, hipStream_t s);
+struct Fp8FwdArgs {
+  const uint8_t *q8, *k8, *vt8;
+  const int32_t *qe, *ke, *ve;
+  uint16_t *o;              // [B, H, N, D] bf16
+  float *lse;               // [B, H, N] or null
+  const int32_t *row_ptr, *col_idx, *row_order;
+  int B, H, N, D, block_q, n_qblk, n_kvblk;
+  float scale_log2;         // log2(e) / sqrt(D)
+};
+hipError_t launch_fwd_fp8(const Fp8FwdArgs &a, hipStream_t s);
 // Tile heatmap, pass 2 (heatmap.hip): per (row, KV block) max and mean mass of exp(s - lse).
 hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
                              int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s);

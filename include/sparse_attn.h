@@ -167,6 +167,47 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
                           int N, int D, const sa_plan *plan, void *dq, void *dk, void *dv,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Low-bit forward (SLA2 page, quantisation-aware fine-tuning: the forward pass runs on
+ * queries, keys and values quantised to low precision). The page names no format; this
+ * library uses OCP FP8 E4M3 (max 448, subnormals down to 2^-9, no infinities) with
+ * power-of-two group scales. A group's exponent e is the smallest integer with
+ * max|x| <= 448 * 2^e, clamped to [-64, 64] (-64 for an all-zero group), and a value x
+ * is stored as the E4M3 code nearest to x * 2^-e, ties to the even code. Groups: q per
+ * (batch, head, query block of block_q tokens), k per (batch, head, 64-key block), v per
+ * (batch, head, channel) over all tokens.
+ *
+ * The pack is one device buffer of sparse_attn_fp8_pack_bytes bytes holding, each part
+ * starting at the next 256-byte boundary after the previous one, in this order:
+ *   q8     uint8 [B, H, N, D]       codes of q, row-major;
+ *   k8     uint8 [B, H, N, D]       codes of k;
+ *   vt8    uint8 [B, H, nKV, D, 64] codes of v, each 64-key block transposed to channel
+ *                                   rows; byte h*32 + b (h in {0, 1}, b < 32) of a row
+ *                                   holds key (b/16)*32 + ((b/4)%4)*8 + h*4 + b%4 of the
+ *                                   block; keys past N hold 0;
+ *   qe     int32 [B, H, nQ]         exponents of the q groups (nQ = ceil(N/block_q));
+ *   ke     int32 [B, H, nKV]        exponents of the k groups (nKV = ceil(N/64));
+ *   ve     int32 [B, H, D]          exponents of the v groups;
+ *   vamax  uint32 [B, H, D]         the quantiser's scratch (per-channel max |v|). */
+size_t sparse_attn_fp8_pack_bytes(int B, int H, int N, int D, int block_q, int block_kv);
+
+/* Quantises q, k, v (device [B, H, N, D] bf16, finite) into pack (device, 256-byte
+ * aligned, pack_bytes >= sparse_attn_fp8_pack_bytes). block_q must be the block_q of the
+ * plans the pack will be used with; block_kv must be 64. fp32 inputs: SA_ERR_UNSUPPORTED.
+ * Deterministic. */
+sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, sa_dtype dtype,
+                                   int B, int H, int N, int D, int block_q, int block_kv,
+                                   void *pack, size_t pack_bytes, hipStream_t stream);
+
+/* Block-sparse attention over the plan's kept tiles computed from an FP8 pack: the
+ * products q k^T and P v run on fp8 MFMA with fp32 accumulation, the softmax in fp32,
+ * and P (the probabilities scaled by 2^8 against the running maximum) is rounded to
+ * E4M3 before it multiplies v; the row sums add the same rounded values.
+ * pack: as sparse_attn_quantize_fp8 wrote it, with the plan's block_q.
+ * plan: a bf16 plan for [B, H, N, D] without a query order (else SA_ERR_UNSUPPORTED).
+ * o: device [B, H, N, D] bf16. lse: device float [B, H, N] or NULL, as sparse_attn_fwd. */
+sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H, int N, int D,
+                              const sa_plan *plan, void *o, float *lse, hipStream_t stream);
+
 /* Ground-truth tile heatmap of full attention (Veda page, section 2.1: the reference mask
  * max-pools the full attention matrix over query x key tiles; section 2.3: two passes).
  * Pass 1 is sparse_attn_fwd on a sparse_attn_plan_dense plan with an lse output; this

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 15
+    assert len(decl) == 18
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -231,3 +231,67 @@ def test_bwd_validation(lib):
     st.q_order = FAKE
     assert call() == E.SA_ERR_UNSUPPORTED                   # ordered plans
     st.q_order = None
+
+
+def _fp8_layout_bytes(B_, H, N, D, bq):
+    """The pack size from the layout the header documents, summed independently."""
+    BH, nQ, nKV = B_ * H, -(-N // bq), -(-N // 64)
+    off = 0
+    for n in (BH * N * D, BH * N * D, BH * nKV * D * 64, 4 * BH * nQ, 4 * BH * nKV, 4 * BH * D, 4 * BH * D):
+        off = (off + n + 255) // 256 * 256
+    return off
+
+
+def test_fp8_pack_bytes(lib):
+    f = lib.sparse_attn_fp8_pack_bytes
+    for shape in ((1, 40, 75600, 128, 128), (1, 12, 32760, 128, 64), (2, 3, 1000, 64, 128)):
+        assert f(*shape, 64) == _fp8_layout_bytes(*shape)
+        p = sa.Fp8Pack(None, shape[:4], shape[4], 64)
+        offs = p._parts()
+        assert offs["vamax"][0] + offs["vamax"][1] <= f(*shape, 64)
+    assert f(1, 1, 1024, 96, 64, 64) == 0
+    assert f(1, 1, 1024, 64, 64, 128) == 0
+
+
+def test_fp8_quantize_and_fwd_validation(lib):
+    need = lib.sparse_attn_fp8_pack_bytes(1, 2, 1024, 64, 64, 64)
+    q = lib.sparse_attn_quantize_fp8
+
+    def quant(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, shape=(1, 2, 1024, 64), bq=64, bk=64, pack=FAKE, pb=need)
+        a.update(kw)
+        return q(a["q"], a["k"], a["v"], a["dt"], *a["shape"], a["bq"], a["bk"], a["pack"], a["pb"], None)
+
+    for name in ("q", "k", "v"):
+        assert quant(**{name: None}) == B.SA_ERR_INVALID_ARG, name
+    assert quant(dt=1) == B.SA_ERR_UNSUPPORTED
+    assert quant(dt=7) == B.SA_ERR_INVALID_ARG
+    assert quant(pb=need - 1) == B.SA_ERR_WORKSPACE
+    assert quant(pack=None) == B.SA_ERR_WORKSPACE
+    assert quant(pack=FAKE + 16) == B.SA_ERR_WORKSPACE
+    assert quant(bk=128) == B.SA_ERR_UNSUPPORTED
+    assert quant(shape=(1, 2, 1024, 80)) == B.SA_ERR_UNSUPPORTED
+
+    st = B.SaPlan()
+    st.B, st.H, st.N, st.D, st.block_q, st.block_kv = 1, 2, 1024, 64, 64, 64
+    st.n_qblk, st.n_kvblk, st.dtype = 16, 16, 0
+    st.row_ptr, st.col_idx, st.row_order = FAKE, FAKE, FAKE
+    f = lib.sparse_attn_fwd_fp8
+
+    def fwd(**kw):
+        a = dict(pack=FAKE, pb=need, shape=(1, 2, 1024, 64), o=FAKE, lse=None)
+        a.update(kw)
+        return f(a["pack"], a["pb"], *a["shape"], ctypes.byref(st), a["o"], a["lse"], None)
+
+    assert fwd(pack=None) == B.SA_ERR_INVALID_ARG
+    assert fwd(o=None) == B.SA_ERR_INVALID_ARG
+    assert fwd(pb=need - 1) == B.SA_ERR_WORKSPACE
+    assert fwd(shape=(1, 2, 2048, 64)) == B.SA_ERR_PLAN_MISMATCH
+    st.dtype = 1
+    assert fwd() == B.SA_ERR_UNSUPPORTED                    # fp32 plans
+    st.dtype = 0
+    st.q_order = FAKE
+    assert fwd() == B.SA_ERR_UNSUPPORTED                    # ordered plans
+    st.q_order = None
+    st.row_ptr = None
+    assert fwd() == B.SA_ERR_INVALID_ARG

@@ -136,3 +136,26 @@ def test_power_of_two_scaling_commutes():
     _, qe, _, ke, _, ve = quantize_qkv(q * 0.25, k, v * 8.0, 64, 64)
     _, qe0, _, _, _, ve0 = quantize_qkv(q, k, v, 64, 64)
     assert np.array_equal(qe, qe0 - 2) and np.array_equal(ve, ve0 + 3)
+
+
+def test_p_rounding_model_below_gpu_bounds():
+    """The model behind the GPU bounds for the low-bit forward: rounding P * 2^8 to E4M3
+    (the kernel's one deliberate rounding after quantisation) moves O, on a seeded case
+    like the GPU tests', by less than half the bounds those tests use (rel-RMS 1e-2, max
+    3% of max |v|)."""
+    import math
+    rng = np.random.default_rng(7)
+    N, D = 512, 64
+    q, k, v = (rng.normal(size=(N, D)) + s for s in (1.0, 1.0, 0.0))
+    k[::97] *= 8.0                                    # sink keys, as the generator's
+    qd, kd, vd = (dequantize(*quantize_qkv(x[None, None], x[None, None], x[None, None], 64, 64), 64, 64)[i][0, 0]
+                  for i, x in enumerate((q, k, v)))
+    s_ = qd @ kd.T / math.sqrt(D)
+    p = np.exp(s_ - s_.max(axis=1, keepdims=True)) * 256.0
+    ph = e4m3_decode(e4m3_encode(p))
+    o = (p @ vd) / p.sum(axis=1, keepdims=True)
+    oh = (ph @ vd) / ph.sum(axis=1, keepdims=True)
+    rr = np.sqrt(((oh - o) ** 2).sum() / (o ** 2).sum())
+    mx = np.abs(oh - o).max() / np.abs(vd).max()
+    assert rr < 0.5e-2 and mx < 0.015, (rr, mx)
+    assert rr > 1e-4                                  # the rounding does act
