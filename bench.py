@@ -154,6 +154,45 @@ def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 20.0):
     }
 
 
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+
+
+def time_fp8(sa, torch, w, dq, dk, dv, p, flops, t_fwd_bf16, args, stream):
+    """Times the low-bit forward over the plan p: the quantiser (Q, K, V to the FP8 pack)
+    and the fp8 attention kernel, each with HIP events on the launch stream."""
+    pack = sa.quantize_fp8(dq, dk, dv, w.block_q)
+    o = torch.empty_like(dq)
+    for _ in range(max(1, args.warmup)):
+        sa.quantize_fp8(dq, dk, dv, w.block_q, out=pack)
+        sa.fwd_fp8(pack, p, out=o)
+    n = max(3, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(stream)
+        sa.quantize_fp8(dq, dk, dv, w.block_q, out=pack)
+        ev[i][1].record(stream)
+        sa.fwd_fp8(pack, p, out=o)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    tq = [e[0].elapsed_time(e[1]) for e in ev]
+    tf = [e[1].elapsed_time(e[2]) for e in ev]
+    t = float(np.mean(tf))
+    log(f"fp8: quantise {np.mean(tq):.3f} ms, forward {t:.3f} ms (bf16 forward {t_fwd_bf16:.3f} ms)")
+    qkv_bytes = 3.0 * w.B * w.H * w.N * w.D * 2
+    return {
+        "ms_quantize": round(float(np.mean(tq)), 4),
+        "ms_fwd_fp8": round(t, 4),
+        "ms_fwd_fp8_median": round(float(np.median(tf)), 4),
+        "ms_fwd_fp8_min": round(float(np.min(tf)), 4),
+        "fwd_fp8_tflops": round(flops / t / 1e9, 2),
+        "fwd_fp8_frac_of_fp8_peak": round(flops / t / 1e9 / PEAK_FP8_TFLOPS, 4),
+        "speedup_fwd_vs_bf16": round(t_fwd_bf16 / t, 3),
+        "quantize_gbs": round(qkv_bytes * 1.5 / (float(np.mean(tq)) * 1e-3) / 1e9, 1),
+        "format": "OCP FP8 E4M3, power-of-two scales: q per query block, k per 64-key block, v per channel",
+    }
+
+
 def time_backward(sa, torch, w, dq, dk, dv, p, pairs, args, stream):
     """Times sparse_attn_bwd over the plan p. Algorithmic work per kept (query, key) pair:
     the recomputed scores, dP = dO V^T, dV, dK and dQ, 2*D flops each (10*D); the kernels
@@ -207,6 +246,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward (dq, dk, dv) over the step's plan, from the "
                          "forward's o and lse and a synthetic upstream gradient")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time the low-bit forward over the step's plan: the FP8 quantiser "
+                         "and the fp8-MFMA attention kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -379,6 +421,10 @@ def main():
         if w.dtype != "bf16" or q_table is not None:
             raise SystemExit("--backward needs a bf16 workload in raster order (no --cubes)")
         out["backward"] = time_backward(sa, torch, w, dq, dk, dv, p, pairs, args, stream)
+    if args.fp8:
+        if w.dtype != "bf16" or q_table is not None:
+            raise SystemExit("--fp8 needs a bf16 workload in raster order (no --cubes)")
+        out["fp8"] = time_fp8(sa, torch, w, dq, dk, dv, p, flops, t_fwd, args, stream)
     if args.copy_probe_mib > 0:
         # a plain copy of known size: HBM counters of this kernel calibrate the others
         nb = args.copy_probe_mib << 20
