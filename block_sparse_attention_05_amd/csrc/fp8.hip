@@ -372,9 +372,9 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
     return intx8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
   };
 
-  auto tile = [&](int J, const char *kt_s, const char *vt_s, auto mask_tag) {
+  auto tile = [&](int J, int ek, const char *kt_s, const char *vt_s, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const float mul = ldexpf(sl2, eq + keb[J]);
+    const float mul = ldexpf(sl2, eq + ek);
     floatx16 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -437,31 +437,53 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
     }
   };
 
+  // Indices and K exponents run ahead of their use: the index of tile it + 2 is fetched
+  // while tile it computes, and the exponent of a tile together with its loads, so no
+  // tile waits on a memory round trip before its loads or its first multiply.
   const int n = end - beg;
   const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
-  issue(cols[0], k0s, v0s);
+  int c_next = n > 1 ? cols[1] : 0;
+  int j_cur = __builtin_amdgcn_readfirstlane(cols[0]);
+  int e_cur = keb[j_cur], e_next = 0, j_next = 0;
+  issue(j_cur, k0s, v0s);
   int it = 0;
   for (; it < n_full; it += 2) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 1 < n) issue(cols[it + 1], k1s, v1s);
-    tile(cols[it], k0s, v0s, std::false_type{});
+    if (it + 1 < n) {
+      j_next = __builtin_amdgcn_readfirstlane(c_next);
+      issue(j_next, k1s, v1s);
+      e_next = keb[j_next];
+    }
+    if (it + 2 < n) c_next = cols[it + 2];
+    tile(j_cur, e_cur, k0s, v0s, std::false_type{});
+    j_cur = j_next;
+    e_cur = e_next;
     if (it + 1 >= n_full) {
       ++it;
       break;
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 2 < n) issue(cols[it + 2], k0s, v0s);
-    tile(cols[it + 1], k1s, v1s, std::false_type{});
+    if (it + 2 < n) {
+      j_next = __builtin_amdgcn_readfirstlane(c_next);
+      issue(j_next, k0s, v0s);
+      e_next = keb[j_next];
+    }
+    if (it + 3 < n) c_next = cols[it + 3];
+    tile(j_cur, e_cur, k1s, v1s, std::false_type{});
+    j_cur = j_next;
+    e_cur = e_next;
   }
   if (n_full < n) {
+    // tile n - 1 (the ragged block) was issued into buffer (n - 1) % 2; j_cur and e_cur
+    // are its index and exponent
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     if ((n - 1) % 2 == 0)
-      tile(cols[n - 1], k0s, v0s, std::true_type{});
+      tile(j_cur, e_cur, k0s, v0s, std::true_type{});
     else
-      tile(cols[n - 1], k1s, v1s, std::true_type{});
+      tile(j_cur, e_cur, k1s, v1s, std::true_type{});
   }
 
   // epilogue: O[q][d] = acc * 2^ev[d] / l, stored bf16

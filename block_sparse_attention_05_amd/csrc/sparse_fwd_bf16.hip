@@ -309,14 +309,19 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // Two tiles per trip so the buffer of each tile is fixed at compile time. Only full
   // tiles run in the loop; the ragged block, when kept, is the row's last tile and runs
   // after it with the key mask.
+  // The kept-block indices run one tile ahead of the loads that use them: the index of
+  // tile it + 2 is fetched while tile it computes, so issuing a tile's loads never waits
+  // on a memory round trip.
   const int n = end - beg;
   const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
+  int c_next = n > 1 ? cols[1] : 0;
   issue(cols[0], k0s, v0s);
   int it = 0;
   for (; it < n_full; it += 2) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 1 < n) issue(cols[it + 1], k1s, v1s);
+    if (it + 1 < n) issue(__builtin_amdgcn_readfirstlane(c_next), k1s, v1s);
+    if (it + 2 < n) c_next = cols[it + 2];
     tile(cols[it], k0s, v0s, std::false_type{});
     if (it + 1 >= n_full) {
       ++it;
@@ -324,7 +329,8 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 2 < n) issue(cols[it + 2], k0s, v0s);
+    if (it + 2 < n) issue(__builtin_amdgcn_readfirstlane(c_next), k0s, v0s);
+    if (it + 3 < n) c_next = cols[it + 3];
     tile(cols[it + 1], k1s, v1s, std::false_type{});
   }
   if (n_full < n) {
