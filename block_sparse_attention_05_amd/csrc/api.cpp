@@ -412,7 +412,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H,
 
 namespace {
 struct BwdLayout {
-  size_t dvec, tbits, ccount, col_ptr, row_idx, total;
+  size_t dvec, lse2, tbits, ccount, col_ptr, row_idx, total;
   int nwq;
 };
 BwdLayout bwd_layout(const Shape &s) {
@@ -426,7 +426,8 @@ BwdLayout bwd_layout(const Shape &s) {
     off = align_up(off + bytes);
     return at;
   };
-  L.dvec = take(BH * (size_t)s.N * 4);
+  L.dvec = take(BH * (size_t)s.nQ * s.bq * 4);
+  L.lse2 = take(BH * (size_t)s.nQ * s.bq * 4);
   L.tbits = take(C * L.nwq * 4);
   L.ccount = take(C * 4);
   L.col_ptr = take((C + 1) * 4);
@@ -467,6 +468,8 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
   a.dout = (const uint16_t *)dout;
   a.lse = lse;
   a.dvec = reinterpret_cast<float *>(ws + L.dvec);
+  a.lse2 = reinterpret_cast<float *>(ws + L.lse2);
+  a.NP = s.nQ * s.bq;
   a.dq = (uint16_t *)dq;
   a.dk = (uint16_t *)dk;
   a.dv = (uint16_t *)dv;

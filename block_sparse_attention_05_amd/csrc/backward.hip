@@ -58,17 +58,24 @@ __device__ __forceinline__ float bf(uint32_t w, int hi) {
 }
 
 // ---------------------------------------------------------------- Dv = rowsum(dO * O)
+// Per head, rows 0 .. NP-1 of the padded arrays: Dv and lse*log2(e) for n < N, and 0 and
+// +inf past N, so that padded query rows get P = 0 and dS = 0 wherever they are read.
 template <int D>
 __global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *__restrict__ o,
-                                                   const uint16_t *__restrict__ dout, long rows,
-                                                   float *__restrict__ dvec) {
+                                                   const uint16_t *__restrict__ dout,
+                                                   const float *__restrict__ lse, int N, int NP, long rows,
+                                                   float *__restrict__ dvec, float *__restrict__ lse2) {
   constexpr int TPR = D / 8;   // lanes per query row
-  const long r = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const long r = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // padded row bh*NP + n
   const int l = threadIdx.x % TPR;
+  const long bh = r / NP;
+  const int n = (int)(r - bh * NP);
+  const bool ok = r < rows && n < N;
   float acc = 0.0f;
-  if (r < rows) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(o + r * D + l * 8);
-    const uint4 b = *reinterpret_cast<const uint4 *>(dout + r * D + l * 8);
+  if (ok) {
+    const long src = bh * N + n;
+    const uint4 a = *reinterpret_cast<const uint4 *>(o + src * D + l * 8);
+    const uint4 b = *reinterpret_cast<const uint4 *>(dout + src * D + l * 8);
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -78,7 +85,10 @@ __global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *__restrict__ 
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m);
-  if (r < rows && l == 0) dvec[r] = acc;
+  if (r < rows && l == 0) {
+    dvec[r] = acc;
+    lse2[r] = ok ? lse[bh * N + n] * kLog2e : INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------- CSC of the mask
@@ -165,9 +175,9 @@ void bwd_dq_kernel(BwdArgs a) {
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
     dof[s] = __builtin_bit_cast(bf16x8_t, x);
   }
-  // a query past N gets lse = +inf, so its P (and dS) is 0
-  const float lse2 = q_ok ? a.lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
-  const float dv = q_ok ? a.dvec[(size_t)bh * N + qi] : 0.0f;
+  // a query past N has lse2 = +inf in the padded array, so its P (and dS) is 0
+  const float lse2 = a.lse2[(size_t)bh * a.NP + qi];
+  const float dv = a.dvec[(size_t)bh * a.NP + qi];
   const float sl2 = a.scale_log2;
 
   uint32_t goff[NIW];
@@ -265,14 +275,17 @@ void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
+  // the index of tile it + 2 loads while tile it computes (no round trip before a tile's loads)
   const int n = end - beg;
   const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
+  int c_next = n > 1 ? cols[1] : 0;
   issue(cols[0], k0s, v0s);
   int it = 0;
   for (; it < n_full; it += 2) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 1 < n) issue(cols[it + 1], k1s, v1s);
+    if (it + 1 < n) issue(__builtin_amdgcn_readfirstlane(c_next), k1s, v1s);
+    if (it + 2 < n) c_next = cols[it + 2];
     tile(cols[it], k0s, v0s, std::false_type{});
     if (it + 1 >= n_full) {
       ++it;
@@ -280,7 +293,8 @@ void bwd_dq_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 2 < n) issue(cols[it + 2], k0s, v0s);
+    if (it + 2 < n) issue(__builtin_amdgcn_readfirstlane(c_next), k0s, v0s);
+    if (it + 3 < n) c_next = cols[it + 3];
     tile(cols[it + 1], k1s, v1s, std::false_type{});
   }
   if (n_full < n) {
@@ -307,25 +321,29 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV (column-major)
-// One workgroup of two waves per KV block (64 keys); each wave owns 32 keys. For every
-// query block that keeps this KV block (the CSC list, ascending), the Q and dO tiles of
-// that block go into LDS, and each 32-query slice contributes
+// One workgroup of two waves per KV block (64 keys); each wave owns 32 keys. The query
+// blocks that keep this KV block (the CSC list, ascending) are walked in stages of 32
+// query rows. A stage's Q and dO rows and its lse*log2(e) and Dv values go HBM -> LDS by
+// direct loads, double-buffered: stage s + 1 loads while stage s computes. Two stages
+// take 38 KB (D = 128), so four workgroups share a CU and each SIMD runs two waves.
+// Each stage contributes
 //   dV^T += dO^T P,  dK^T += Q^T dS   (then dK is scaled by c).
 template <int D, int BQ>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = 2;
-  constexpr int GR = D / 8 + 1;
+  constexpr int SR = 32;                     // query rows per stage
+  constexpr int SPB = BQ / SR;               // stages per query block
+  constexpr int GR = D / 8 + 1;              // 16-byte granules per padded LDS row
   constexpr int ROWB = GR * 16;
-  constexpr int NIQ = BQ * GR / 64;          // 1 KB direct loads per BQ-row tile
+  constexpr int NIQ = (SR * GR + 63) / 64;   // 1 KB direct loads per Q (or dO) tile
   constexpr int NIQW = (NIQ + NW - 1) / NW;
+  constexpr int TILEB = NIQ * 1024;          // the tile's SR*ROWB bytes, then spare for the last load
+  constexpr int STAGE = 2 * TILEB + 1024;    // Q, dO, lse2 (128 B), Dv (128 B), spare
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
 
-  __shared__ __align__(16) char qs_[BQ * ROWB];
-  __shared__ __align__(16) char dos_[BQ * ROWB];
-  __shared__ __align__(16) float lse_s[BQ];
-  __shared__ __align__(16) float dv_s[BQ];
+  __shared__ __align__(16) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -341,6 +359,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const size_t head = (size_t)bh * N * D;
   const uint16_t *qg = a.q + head;
   const uint16_t *dog = a.dout + head;
+  const float *lse2g = a.lse2 + (size_t)bh * a.NP;
+  const float *dvg = a.dvec + (size_t)bh * a.NP;
   const int key = J * kBk + wid * 32 + l32;
   const bool k_ok = key < N;
 
@@ -356,6 +376,54 @@ void bwd_dkdv_kernel(BwdArgs a) {
     vf[s] = __builtin_bit_cast(bf16x8_t, x);
   }
   const float sl2 = a.scale_log2;
+
+  // direct-load sources within a stage: load i fills LDS granules 64i .. 64i+63 of the
+  // padded tile; lane p carries granule (row (64i+p)/GR, column (64i+p)%GR), the pad
+  // column reloading column 0. Granules past the tile's SR rows land in its spare bytes
+  // and read row SR - 1. Wave w issues loads w, w + NW, ... of Q and of dO.
+  uint32_t toffs[NIQW];
+#pragma unroll
+  for (int m = 0; m < NIQW; ++m) {
+    const int p = 64 * (wid + m * NW) + lane;
+    const int c = p % GR;
+    toffs[m] = (min(p / GR, SR - 1) * D + (c < D / 8 ? c : 0) * 8) * 2;
+  }
+  // the lse2 / Dv load: lanes 0..7 carry lse2, 8..15 Dv, 16..63 repeat them into the spare
+  const int lv = lane & 15;
+  const float *ldsrc = (lv < 8 ? lse2g : dvg) + 4 * (lv & 7);
+
+  auto issue = [&](int q0, char *buf) {
+    const char *qb = reinterpret_cast<const char *>(qg + (size_t)q0 * D);
+    const char *db = reinterpret_cast<const char *>(dog + (size_t)q0 * D);
+    if (q0 + SR <= N) {
+#pragma unroll
+      for (int m = 0; m < NIQW; ++m) {
+        const int i = wid + m * NW;
+        if (i < NIQ) {
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(qb + toffs[m]), (lvoid_t *)(buf + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(db + toffs[m]), (lvoid_t *)(buf + TILEB + i * 1024), 16, 0, 0);
+        }
+      }
+    } else {
+      // rows past N reload row N - 1 (in bounds; their lse2 is +inf, so they add nothing)
+#pragma unroll
+      for (int m = 0; m < NIQW; ++m) {
+        const int i = wid + m * NW;
+        if (i < NIQ) {
+          const int p = 64 * i + lane;
+          const int c = p % GR;
+          const int grow = min(q0 + min(p / GR, SR - 1), N - 1);
+          const size_t off = ((size_t)grow * D + (c < D / 8 ? c : 0) * 8) * 2;
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(reinterpret_cast<const char *>(qg) + off),
+                                           (lvoid_t *)(buf + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gvoid_t *)(reinterpret_cast<const char *>(dog) + off),
+                                           (lvoid_t *)(buf + TILEB + i * 1024), 16, 0, 0);
+        }
+      }
+    }
+    if (wid == NW - 1)   // q0 + SR <= NP: the padded arrays cover the whole stage
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(ldsrc + q0), (lvoid_t *)(buf + 2 * TILEB), 16, 0, 0);
+  };
 
   const int qoff = l32 * ROWB + hf * 16;     // row reads of Q and dO (A operands of S, dP)
   const int u = lane & 15;
@@ -373,35 +441,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
       dvacc[t][i] = 0.0f;
     }
 
-  const int cbeg = a.col_ptr[col], cend = a.col_ptr[col + 1];
-  for (int x = cbeg; x < cend; ++x) {
-    const int I = a.row_idx[x];
-    const int q0 = I * BQ;
-    const int last = N - 1 - q0;             // last valid row of this query block
-    __syncthreads();                         // the previous block's tiles are consumed
-    const char *qb = reinterpret_cast<const char *>(qg + (size_t)q0 * D);
-    const char *db = reinterpret_cast<const char *>(dog + (size_t)q0 * D);
+  auto compute = [&](const char *cur) {
+    const char *qs_ = cur;
+    const char *dos_ = cur + TILEB;
+    const float *lse_s = reinterpret_cast<const float *>(cur + 2 * TILEB);
+    const float *dv_s = lse_s + SR;
 #pragma unroll
-    for (int m = 0; m < NIQW; ++m) {
-      const int i = wid + m * NW;
-      if (i < NIQ) {
-        const int p = 64 * i + lane;
-        const int c = p % GR;
-        const uint32_t off = (min(p / GR, last) * D + (c < D / 8 ? c : 0) * 8) * 2;
-        __builtin_amdgcn_global_load_lds((gvoid_t *)(qb + off), (lvoid_t *)(qs_ + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid_t *)(db + off), (lvoid_t *)(dos_ + i * 1024), 16, 0, 0);
-      }
-    }
-    for (int t = tid; t < BQ; t += 64 * NW) {
-      const bool ok = q0 + t < N;
-      lse_s[t] = ok ? a.lse[(size_t)bh * N + q0 + t] * kLog2e : INFINITY;   // P = 0 past N
-      dv_s[t] = ok ? a.dvec[(size_t)bh * N + q0 + t] : 0.0f;
-    }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-
-#pragma unroll
-    for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
+    for (int qb2 = 0; qb2 < SR / 32; ++qb2) {
       floatx16 sacc, dpacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -421,11 +467,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const float4 l4 = *reinterpret_cast<const float4 *>(&lse_s[qb2 * 32 + g * 8 + hf * 4]);
         const float4 d4 = *reinterpret_cast<const float4 *>(&dv_s[qb2 * 32 + g * 8 + hf * 4]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lv4[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = g * 4 + r;
-          p[i] = __builtin_amdgcn_exp2f(sacc[i] * sl2 - lv[r]);
+          p[i] = __builtin_amdgcn_exp2f(sacc[i] * sl2 - lv4[r]);
           ds[i] = p[i] * (dpacc[i] - dvv[r]);
         }
       }
@@ -454,6 +500,23 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
+  };
+
+  // stage s covers query rows I*BQ + (s % SPB)*SR .. +SR-1 of I = row_idx[cbeg + s / SPB];
+  // the block index of stage s + 2 loads while stage s computes
+  const int cbeg = a.col_ptr[col], cend = a.col_ptr[col + 1];
+  const int nst = (cend - cbeg) * SPB;
+  if (nst > 0) {
+    int i_next = nst > 1 ? a.row_idx[cbeg + 1 / SPB] : 0;
+    issue(__builtin_amdgcn_readfirstlane(a.row_idx[cbeg]) * BQ, smem);
+    for (int st = 0; st < nst; ++st) {
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();   // stage st has landed; every wave is done with stage st - 1's buffer
+      if (st + 1 < nst)
+        issue(__builtin_amdgcn_readfirstlane(i_next) * BQ + ((st + 1) % SPB) * SR, smem + ((st + 1) & 1) * STAGE);
+      if (st + 2 < nst) i_next = a.row_idx[cbeg + (st + 2) / SPB];
+      compute(smem + (st & 1) * STAGE);
+    }
   }
 
   if (k_ok) {
@@ -477,13 +540,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s) {
   const int BH = a.B * a.H;
-  const long rows = (long)BH * a.N;
+  const long rows = (long)BH * a.NP;
   hipError_t e;
-  // Dv
+  // Dv and lse * log2(e), padded per head to NP rows
   if (a.D == 128)
-    dvec_kernel<128><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a.o, a.dout, rows, a.dvec);
+    dvec_kernel<128><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a.o, a.dout, a.lse, a.N, a.NP, rows, a.dvec,
+                                                                  a.lse2);
   else
-    dvec_kernel<64><<<(unsigned)((rows + 31) / 32), 256, 0, s>>>(a.o, a.dout, rows, a.dvec);
+    dvec_kernel<64><<<(unsigned)((rows + 31) / 32), 256, 0, s>>>(a.o, a.dout, a.lse, a.N, a.NP, rows, a.dvec,
+                                                                 a.lse2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // CSC of the mask
   const int R = BH * a.n_qblk;

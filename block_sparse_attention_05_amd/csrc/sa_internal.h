@@ -75,7 +75,9 @@ hipError_t launch_cube_order(int H, int T, int Hg, int W, const CubeTable &cubes
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;   // [B, H, N, D] bf16
   const float *lse;                        // [B, H, N] from the forward
-  float *dvec;                             // [B, H, N] workspace: rowsum(dO * O)
+  float *dvec;                             // [B*H, NP] workspace: rowsum(dO * O), 0 past N
+  float *lse2;                             // [B*H, NP] workspace: lse * log2(e), +inf past N
+  int NP;                                  // n_qblk * block_q (per-head padded length)
   uint16_t *dq, *dk, *dv;                  // [B, H, N, D] bf16
   const int32_t *row_ptr, *col_idx, *row_order;
   int32_t *col_ptr, *row_idx;              // CSC of the mask (workspace)
