@@ -2,7 +2,9 @@
 
 One step = sparse_attn_plan (pool, scores, hybrid top-k/top-p select, CSR) followed by
 sparse_attn_fwd over the kept tiles, on seeded synthetic video-token Q, K, V already
-resident in HBM. Prints one JSON line:
+resident in HBM. By default the step goes through sparse_attn_pipelined, which runs the
+two over chunks of heads on two streams (--chunks, 4); the plain plan-then-forward
+sequence is timed as well (ms_step_sequential, ms_plan, ms_fwd). Prints one JSON line:
 
   value        effective TFLOP/s over the exact kept query-key pairs (4*D flops per
                pair) per step, plan included
@@ -243,6 +245,10 @@ def main():
     ap.add_argument("--quality", action="store_true",
                     help="also build the ground-truth tile heatmap of full attention (two "
                          "passes) and report the router mask's recall and retained mass")
+    ap.add_argument("--chunks", type=int, default=4,
+                    help="heads per step are split into this many chunks, pipelined over two "
+                         "streams (plan of one chunk overlapping the forward of the previous); "
+                         "0 times the plain plan-then-forward sequence as the step")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward (dq, dk, dv) over the step's plan, from the "
                          "forward's o and lse and a synthetic upstream gradient")
@@ -341,6 +347,32 @@ def main():
     t_fwd = float(np.mean(ms_fwd))
     t_plan = float(np.mean(ms_plan))
     log(f"step {t_step:.3f} ms (plan {t_plan:.3f}, fwd {t_fwd:.3f}); wall {1e3 * wall / args.steps:.3f} ms/step")
+    t_seq = t_step
+    ms_seq = ms_step
+    pipelined = args.chunks > 0 and q_table is None and not w.linear
+    if pipelined:
+        # the step through the pipelined call: plan + forward over head chunks, two streams
+        pws = torch.empty(sa.pipelined_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv, args.chunks),
+                          dtype=torch.uint8, device="cuda")
+
+        def pstep():
+            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=args.chunks, out=o,
+                         workspace=pws)
+        for _ in range(args.warmup):
+            pstep()
+        p0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        p1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        pw0 = time.perf_counter()
+        for i in range(args.steps):
+            p0[i].record(stream)
+            pstep()
+            p1[i].record(stream)
+        torch.cuda.synchronize()
+        pwall = time.perf_counter() - pw0
+        ms_step = [a.elapsed_time(b) for a, b in zip(p0, p1)]
+        t_step = float(np.mean(ms_step))
+        log(f"pipelined step ({args.chunks} chunks) {t_step:.3f} ms; wall {1e3 * pwall / args.steps:.3f} ms/step")
 
     res_extra = {}
     if not args.no_dense:
@@ -389,10 +421,14 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "grid": list(w.grid),
             "block_q": w.block_q, "block_kv": w.block_kv, "topk": w.topk, "top_p": w.top_p,
             "linear_branch": bool(w.linear),
+            "pipeline": ({"chunks": args.chunks, "streams": 2, "call": "sparse_attn_pipelined"}
+                         if pipelined else None),
             "cube_tiling": ({"query_cubes": Q_CUBES, "key_cubes": KV_CUBES, "per_head": "h mod 3",
                              "moved": "k, v (q and o through the plan's query order)"}
                             if args.cubes else None),
         },
+        "ms_step_sequential": round(t_seq, 4),
+        "ms_step_sequential_median": round(float(np.median(ms_seq)), 4),
         "ms_plan": round(t_plan, 4),
         "ms_fwd": round(t_fwd, 4),
         "ms_step_median": round(float(np.median(ms_step)), 4),

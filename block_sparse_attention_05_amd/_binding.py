@@ -25,6 +25,7 @@ EXPORTS = (
     "sparse_attn_plan_workspace_bytes", "sparse_attn_plan", "sparse_attn_plan_dense",
     "sparse_attn_plan_from_csr", "sparse_attn_fwd_workspace_bytes", "sparse_attn_fwd",
     "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd",
+    "sparse_attn_pipelined_workspace_bytes", "sparse_attn_pipelined",
     "sparse_attn_plan_ordered", "sparse_attn_tile_stats", "sparse_attn_cube_permute",
     "sparse_attn_cube_order", "sparse_attn_fp8_pack_bytes", "sparse_attn_quantize_fp8",
     "sparse_attn_fwd_fp8", "sparse_attn_router_exp", "sparse_attn_status_string",
@@ -88,6 +89,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp,
                                     vp, sz, vp]
     lib.sparse_attn_bwd.restype = i32
+    lib.sparse_attn_pipelined_workspace_bytes.argtypes = [i32] * 7
+    lib.sparse_attn_pipelined_workspace_bytes.restype = sz
+    lib.sparse_attn_pipelined.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [dbl, dbl, i32, vp, vp, vp, sz, vp, vp]
+    lib.sparse_attn_pipelined.restype = i32
     lib.sparse_attn_fp8_pack_bytes.argtypes = [i32] * 6
     lib.sparse_attn_fp8_pack_bytes.restype = sz
     lib.sparse_attn_quantize_fp8.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [vp, sz, vp]
@@ -433,6 +438,48 @@ def fwd_fp8(pack: Fp8Pack, plan: Plan, return_lse: bool = False, out=None, lse=N
     _check(lib.sparse_attn_fwd_fp8(pack.buf.data_ptr(), pack.buf.numel(), B, H, N, D, ctypes.byref(plan.st),
                                    o.data_ptr(), lse.data_ptr() if return_lse else None, _stream(stream)),
            "sparse_attn_fwd_fp8")
+    return (o, lse) if return_lse else o
+
+
+_AUX = {}
+
+
+def _aux_stream(device):
+    """One auxiliary stream per device, at the default priority, made once."""
+    torch = _torch()
+    key = torch.device(device).index
+    if key not in _AUX:
+        _AUX[key] = torch.cuda.Stream(device=device)
+    return _AUX[key]
+
+
+def pipelined_workspace_bytes(B, H, N, D, block_q=128, block_kv=64, chunks=4) -> int:
+    return int(load_library().sparse_attn_pipelined_workspace_bytes(B, H, N, D, block_q, block_kv, chunks))
+
+
+def attention(q, k, v, block_q: int = 128, block_kv: int = 64, topk: float = 0.05, top_p: float = 0.9,
+              chunks: int = 4, return_lse: bool = False, out=None, lse=None, workspace=None, stream=None,
+              aux_stream=None):
+    """Plan and forward for all heads in one call, pipelined over chunks of heads on two
+    streams (see sparse_attn_pipelined). Returns o (and lse with return_lse)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    need = lib.sparse_attn_pipelined_workspace_bytes(B, H, N, D, block_q, block_kv, chunks)
+    if need == 0:
+        raise SparseAttnError(SA_ERR_UNSUPPORTED, "pipelined shape")
+    ws = workspace if workspace is not None else _new_ws(need, q.device)
+    o = out if out is not None else torch.empty_like(q)
+    _check_qkv(q, o)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    aux = aux_stream if aux_stream is not None else _aux_stream(q.device)
+    _check(lib.sparse_attn_pipelined(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, N, D,
+                                     block_q, block_kv, float(topk), float(top_p), int(chunks), o.data_ptr(),
+                                     lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(),
+                                     s.cuda_stream, aux.cuda_stream), "sparse_attn_pipelined")
     return (o, lse) if return_lse else o
 
 

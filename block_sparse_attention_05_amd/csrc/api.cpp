@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "sa_internal.h"
@@ -318,6 +319,102 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
     a.ol = lb.ol;
   }
   return hip_status(launch_fwd(a, dtype, stream));
+}
+
+namespace {
+// The pipelined call splits the B*H heads into chunks of `per` heads, each planned in its
+// own plan workspace.
+struct PipeLayout {
+  int C, per;
+  size_t plan_bytes, total;
+};
+sa_status pipe_layout(int B, int H, int N, int D, int bq, int bk, int n_chunks, PipeLayout *L) {
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, bq, bk, &s);
+  if (st != SA_OK) return st;
+  if (n_chunks < 1) return SA_ERR_INVALID_ARG;
+  const int BH = B * H;
+  L->per = ceil_div(BH, n_chunks < BH ? n_chunks : BH);
+  L->C = ceil_div(BH, L->per);
+  Shape s1;
+  st = check_shape(1, L->per, N, D, bq, bk, &s1);
+  if (st != SA_OK) return st;
+  L->plan_bytes = plan_layout(s1).total;
+  L->total = L->plan_bytes * L->C;
+  return SA_OK;
+}
+}  // namespace
+
+size_t sparse_attn_pipelined_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv,
+                                             int n_chunks) {
+  PipeLayout L;
+  if (pipe_layout(B, H, N, D, block_q, block_kv, n_chunks, &L) != SA_OK) return 0;
+  return L.total;
+}
+
+sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_dtype dtype, int B, int H,
+                                int N, int D, int block_q, int block_kv, double topk_frac, double top_p,
+                                int n_chunks, void *o, float *lse, void *workspace, size_t ws_bytes,
+                                hipStream_t stream, hipStream_t aux_stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  if (!(topk_frac >= 0.0 && topk_frac <= 1.0) || !(top_p >= 0.0 && top_p <= 1.0)) return SA_ERR_INVALID_ARG;
+  PipeLayout L;
+  sa_status st = pipe_layout(B, H, N, D, block_q, block_kv, n_chunks, &L);
+  if (st != SA_OK) return st;
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != SA_OK) return st;
+
+  const int BH = B * H;
+  const size_t esz = dtype == SA_BF16 ? 2 : 4;
+  const size_t head_bytes = (size_t)N * D * esz;
+  auto chunk = [&](int c, const char *base) { return base + (size_t)c * L.per * head_bytes; };
+  const bool two = aux_stream != stream;
+  // Plans go on aux_stream back to back; forwards on `stream`, each after its chunk's plan.
+  // Only the first plan is exposed; the others run under the forwards before them.
+  std::vector<hipEvent_t> ev;
+  auto release = [&]() {
+    for (hipEvent_t e : ev) hipEventDestroy(e);   // released once the device is done with them
+  };
+  if (two) {
+    ev.resize(L.C + 1, nullptr);
+    for (auto &e : ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        e = nullptr;
+        st = SA_ERR_HIP;
+      }
+    // the plans start after the caller's earlier work on `stream` (inputs written there)
+    if (st == SA_OK && (hipEventRecord(ev[L.C], stream) != hipSuccess ||
+                        hipStreamWaitEvent(aux_stream, ev[L.C], 0) != hipSuccess))
+      st = SA_ERR_HIP;
+    if (st != SA_OK) {
+      ev.erase(std::remove(ev.begin(), ev.end(), nullptr), ev.end());
+      release();
+      return st;
+    }
+  }
+  std::vector<sa_plan> plans(L.C);
+  for (int c = 0; c < L.C && st == SA_OK; ++c) {
+    const int hc = BH - c * L.per < L.per ? BH - c * L.per : L.per;
+    char *ws = static_cast<char *>(workspace) + c * L.plan_bytes;
+    st = plan_impl(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)), dtype, 1, hc,
+                   N, D, block_q, block_kv, topk_frac, top_p, nullptr, ws, L.plan_bytes, &plans[c],
+                   two ? aux_stream : stream);
+    if (st == SA_OK && two && hipEventRecord(ev[c], aux_stream) != hipSuccess) st = SA_ERR_HIP;
+  }
+  for (int c = 0; c < L.C && st == SA_OK; ++c) {
+    const int hc = BH - c * L.per < L.per ? BH - c * L.per : L.per;
+    if (two && hipStreamWaitEvent(stream, ev[c], 0) != hipSuccess) {
+      st = SA_ERR_HIP;
+      break;
+    }
+    float *lc = lse ? lse + (size_t)c * L.per * N : nullptr;
+    st = sparse_attn_fwd(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)),
+                         chunk(c, static_cast<const char *>(v)), dtype, 1, hc, N, D, &plans[c], nullptr,
+                         const_cast<char *>(chunk(c, static_cast<const char *>(o))), lc, nullptr, 0, stream);
+  }
+  release();
+  return st;
 }
 
 namespace {

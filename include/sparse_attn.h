@@ -150,6 +150,30 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
                           const float *alpha, void *o, float *lse,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes sparse_attn_pipelined needs: one plan workspace per chunk of heads. */
+size_t sparse_attn_pipelined_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv,
+                                             int n_chunks);
+
+/* The two hot-path calls, sparse_attn_plan then sparse_attn_fwd (without the linear
+ * branch), for all B*H heads, pipelined over chunks of heads: the B*H (batch, head)
+ * pairs are split into ceil(B*H / ceil(B*H / n_chunks)) chunks of consecutive pairs.
+ * The chunks' plans run back to back on aux_stream and their forwards on `stream`, each
+ * forward after its chunk's plan, so every plan but the first (a chain of small,
+ * latency-bound kernels) runs under the forwards of earlier chunks. A head's mask depends
+ * on that head alone, so o and lse equal those of the two-call path bit for bit.
+ * Ordering: the plans on aux_stream start after the work enqueued on `stream` before this
+ * call; every forward is on `stream`, so later work there follows them. aux_stream may
+ * equal stream (plans and forwards then run in order). The plans live in the workspace and
+ * are not returned; a caller that needs the mask (for the backward) uses the two calls.
+ * q, k, v, o, lse, dtype, block sizes, topk_frac and top_p as for sparse_attn_plan and
+ * sparse_attn_fwd; n_chunks >= 1 (values above B*H act as B*H).
+ * workspace: sparse_attn_pipelined_workspace_bytes bytes, 256-byte aligned. */
+sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_dtype dtype,
+                                int B, int H, int N, int D, int block_q, int block_kv,
+                                double topk_frac, double top_p, int n_chunks, void *o,
+                                float *lse, void *workspace, size_t ws_bytes,
+                                hipStream_t stream, hipStream_t aux_stream);
+
 /* Workspace bytes sparse_attn_bwd needs for this shape. */
 size_t sparse_attn_bwd_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv);
 

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 18
+    assert len(decl) == 20
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -295,3 +295,32 @@ def test_fp8_quantize_and_fwd_validation(lib):
     st.q_order = None
     st.row_ptr = None
     assert fwd() == B.SA_ERR_INVALID_ARG
+
+
+def test_pipelined_validation(lib):
+    f = lib.sparse_attn_pipelined_workspace_bytes
+    one = lib.sparse_attn_plan_workspace_bytes(1, 5, 75600, 128, 128, 64)
+    assert f(1, 40, 75600, 128, 128, 64, 8) == 8 * one          # eight chunks of five heads
+    assert f(2, 3, 1000, 64, 64, 64, 4) == 3 * lib.sparse_attn_plan_workspace_bytes(1, 2, 1000, 64, 64, 64)
+    assert f(1, 4, 1000, 64, 64, 64, 100) == 4 * lib.sparse_attn_plan_workspace_bytes(1, 1, 1000, 64, 64, 64)
+    assert f(1, 4, 1000, 64, 64, 64, 0) == 0
+    assert f(1, 4, 1000, 80, 64, 64, 2) == 0
+    need = f(1, 2, 1024, 64, 64, 64, 2)
+    g = lib.sparse_attn_pipelined
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, shape=(1, 2, 1024, 64), bq=64, bk=64, k_=0.1, p=0.9, C=2,
+                 o=FAKE, lse=None, ws=FAKE, wsb=need)
+        a.update(kw)
+        return g(a["q"], a["k"], a["v"], a["dt"], *a["shape"], a["bq"], a["bk"], a["k_"], a["p"], a["C"],
+                 a["o"], a["lse"], a["ws"], a["wsb"], None, None)
+
+    for name in ("q", "k", "v", "o"):
+        assert call(**{name: None}) == B.SA_ERR_INVALID_ARG, name
+    assert call(dt=5) == B.SA_ERR_INVALID_ARG
+    assert call(k_=1.5) == B.SA_ERR_INVALID_ARG
+    assert call(p=-0.1) == B.SA_ERR_INVALID_ARG
+    assert call(C=0) == B.SA_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == B.SA_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == B.SA_ERR_WORKSPACE
+    assert call(bk=128) == B.SA_ERR_UNSUPPORTED

@@ -1,0 +1,61 @@
+"""The pipelined call (plan + forward over chunks of heads on two streams) against the
+two-call path: a head's mask and output depend on that head alone, so o and lse must be
+equal bit for bit for every chunking, including chunks that cut a batch's heads and a
+last chunk shorter than the others."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_05_amd as sa
+import workloads as W
+from tests.gpu_common import inputs, log
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, H, N, D, dtype, block_q, topk, top_p, chunks
+    ("pipe_b2h3_c4", 2, 3, 1000, 64, "bf16", 64, 0.1, 0.9, 4),
+    ("pipe_h5_c2", 1, 5, 3000, 128, "bf16", 128, 0.05, 0.9, 2),
+    ("pipe_h4_c8", 1, 4, 2048, 128, "bf16", 128, 0.1, 0.85, 8),
+    ("pipe_fp32_c3", 1, 3, 700, 64, "fp32", 64, 0.25, 0.9, 3),
+]
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pipelined_equals_two_calls(case):
+    name, B, H, N, D, dt, bq, topk, p, C = case
+    w = W.Workload(name, B, H, D, (1, 1, N), dt, bq, 64, topk, p, 4, seed=5)
+    ent = inputs(w)
+    plan = sa.plan(ent["dq"], ent["dk"], bq, 64, topk, p)
+    o1, l1 = sa.fwd(ent["dq"], ent["dk"], ent["dv"], plan, return_lse=True)
+    o2, l2 = sa.attention(ent["dq"], ent["dk"], ent["dv"], bq, 64, topk, p, chunks=C, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o1), _bits(o2)), "o"
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "lse"
+    # one stream for both: the chunks run in order
+    s = torch.cuda.current_stream()
+    o3 = sa.attention(ent["dq"], ent["dk"], ent["dv"], bq, 64, topk, p, chunks=C, stream=s, aux_stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o1), _bits(o3)), "o, one stream"
+    log(f"{name}: pipelined over {C} chunks equals the two-call path bitwise")
+
+
+def test_pipelined_orders_with_caller_stream():
+    """Work the caller enqueues after the call sees the finished output, and the call sees
+    the caller's earlier writes (inputs overwritten right before the call)."""
+    w = W.Workload("pipe_order", 1, 6, 64, (1, 1, 1500), "bf16", 64, 64, 0.1, 0.9, 4, seed=6)
+    ent = inputs(w)
+    q = torch.zeros_like(ent["dq"])
+    ref = sa.attention(ent["dq"], ent["dk"], ent["dv"], 64, 64, 0.1, 0.9, chunks=6)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        q.zero_()
+        q.copy_(ent["dq"])                       # enqueued on the current stream
+        o = sa.attention(q, ent["dk"], ent["dv"], 64, 64, 0.1, 0.9, chunks=6)
+        snap = o.clone()                         # enqueued after the call
+        torch.cuda.synchronize()
+        assert torch.equal(snap.view(torch.int16), ref.view(torch.int16))
