@@ -3,6 +3,7 @@ heatmap) on hand-made rows."""
 import numpy as np
 
 import bench
+import workloads as W
 
 
 def test_mask_quality_hand_rows():
@@ -28,3 +29,17 @@ def test_mask_quality_ties_rank_lower_index_first():
     q = bench.mask_quality(tmax, tmass, np.array([0, 1]), np.array([0]))
     assert q["recall_max"]["mean"] == 1.0      # block 0 wins the three-way tie
     assert q["recall_mass"]["mean"] == 0.0     # block 2 holds the most mass
+
+
+def test_cpu_baseline_walks_heads_within_budget():
+    """The CPU baseline leg: whole heads of the oracle's output track until the budget is
+    used."""
+    from oracle import oracle_plan
+    w = W.CONFIGS["tiny_fp32"]
+    q, k, v, _ = W.make_inputs(w)
+    rp, ci, _ = oracle_plan(W.to_f32(q), W.to_f32(k), w.block_q, w.block_kv, w.topk, w.top_p)
+    res = bench.cpu_baseline(w, q, k, v, rp, ci, budget_s=1e9)
+    assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
+    assert f"heads 0..{w.H - 1}" in res["sample"]
+    one = bench.cpu_baseline(w, q, k, v, rp, ci, budget_s=0.0)     # stops after the first head
+    assert "heads 0..0" in one["sample"]
