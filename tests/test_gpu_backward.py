@@ -9,9 +9,10 @@ sums many such terms with mixed signs, so the bound is rel-RMS 1e-2 and max |d| 
 3e-2 of the largest reference magnitude. The second is the exact gradient. There the
 rounding of o to bf16 also enters: it shifts Dv, and dQ = c * sum_j dS_ij k_j turns that
 shift into c * dDv_i * sum_j P_ij k_j, which the keys' shared components (positional
-term, sinks) do not cancel. On the small ragged case the oracle alone shows dQ off by
-rel-RMS 1.07e-2 from this source, so dQ is held to rel-RMS 2e-2 against the exact
-gradient. Zero gradients (empty rows, KV blocks no row keeps) must be exactly zero.
+term, sinks) do not cancel. Its size depends on the case (rel-RMS 1.1e-2 on the small
+ragged case, 3.4e-2 when 37 tokens share one block), and the oracle gives it exactly:
+by the triangle inequality the kernel is within that distance plus its own bounds
+(rel-RMS 1e-2, max 3%) of the exact gradient. Zero gradients (empty rows, KV blocks no row keeps) must be exactly zero.
 """
 import numpy as np
 import pytest
@@ -26,7 +27,6 @@ pytestmark = pytest.mark.gpu
 
 TOL_RRMS = 1e-2
 TOL_MAX_REL = 3e-2
-TOL_RRMS_EXACT_DQ = 2e-2
 
 
 def _dout(w, seed=7):
@@ -34,7 +34,7 @@ def _dout(w, seed=7):
     return W.f64_to_bf16_bits(rng.normal(size=(w.B, w.H, w.N, w.D)))
 
 
-def _check(got, ref, what, mask=None, rrms=TOL_RRMS):
+def _check(got, ref, what, mask=None, rrms=TOL_RRMS, max_extra=0.0):
     g = to_f64(got)
     if mask is not None:
         g, ref = g[mask], ref[mask]
@@ -44,7 +44,7 @@ def _check(got, ref, what, mask=None, rrms=TOL_RRMS):
     mx = float(err.max())
     assert np.all(np.isfinite(g)), f"{what}: non-finite"
     assert rr <= rrms, f"{what}: rel-RMS {rr:.3e}"
-    assert mx <= TOL_MAX_REL * scale, f"{what}: max |d| {mx:.3e} vs max |ref| {scale:.3e}"
+    assert mx <= TOL_MAX_REL * scale + max_extra, f"{what}: max |d| {mx:.3e} vs max |ref| {scale:.3e}"
     return rr, mx / scale
 
 
@@ -54,6 +54,8 @@ CASES = [
     ("bwd_d128_q128_ragged", 2, 2, 3000, 128, 128, 0.05, 0.9),
     ("bwd_d128_q64", 1, 2, 2048, 128, 64, 0.1, 0.85),
     ("bwd_d64_q128", 1, 3, 1536, 64, 128, 0.1, 0.7),
+    ("bwd_n37", 1, 2, 37, 64, 64, 0.5, 0.9),
+    ("bwd_n100_q128", 1, 2, 100, 128, 128, 0.5, 0.9),
 ]
 
 
@@ -75,9 +77,12 @@ def test_bwd_small(case):
     args = (ent["q32"], ent["k32"], W.to_f32(ent["v"]), W.to_f32(do), rp, ci, bq, 64)
     rq, rk, rv = sparse_attention_backward(*args, o=o)
     e = [_check(gq, rq, "dq"), _check(gk, rk, "dk"), _check(gv, rv, "dv")]
-    xq, xk, xv = sparse_attention_backward(*args)
-    x = [_check(gq, xq, "dq exact", rrms=TOL_RRMS_EXACT_DQ), _check(gk, xk, "dk exact"),
-         _check(gv, xv, "dv exact")]
+    exact = sparse_attention_backward(*args)
+    x = []
+    for g, st, ex, what in zip((gq, gk, gv), (rq, rk, rv), exact, ("dq", "dk", "dv")):
+        inherent = float(np.sqrt(((st - ex) ** 2).sum()) / np.sqrt((ex ** 2).sum()))   # bf16 o alone
+        x.append(_check(g, ex, what + " exact", rrms=inherent + TOL_RRMS,
+                        max_extra=float(np.abs(st - ex).max())))
     log(f"{name}: nnz {rp[-1]}; rel-RMS / max rel vs the stored-o reference: " +
         ", ".join(f"{a:.1e}/{b:.1e}" for a, b in e) + "; vs exact: " +
         ", ".join(f"{a:.1e}/{b:.1e}" for a, b in x))

@@ -37,6 +37,7 @@ CASES = [
     ("fp8_d128_q128_ragged", 2, 2, 3000, 128, 128, 0.05, 0.9),
     ("fp8_d128_q64", 1, 2, 2048, 128, 64, 0.1, 0.85),
     ("fp8_d64_q128", 1, 3, 1536, 64, 128, 0.1, 0.7),
+    ("fp8_n37", 1, 2, 37, 128, 128, 0.5, 0.9),
 ]
 
 

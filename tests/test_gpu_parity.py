@@ -14,7 +14,7 @@ import block_sparse_attention_05_amd as sa
 import workloads as W
 from oracle import (oracle_plan, sparse_attention, dense_attention, dense_plan, exp_sa,
                     topk_count)
-from tests.gpu_common import check_out, inputs, log, sample_rows, to_dev, to_f64
+from tests.gpu_common import drop, check_out, inputs, log, sample_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,10 @@ SMALL = [
     ("nkv300", 1, 2, 64 * 300 - 5, 128, "bf16", 128, 0.03, 0.95),
     ("nkv1100", 1, 1, 64 * 1100 + 7, 128, "bf16", 128, 0.02, 0.85),
     ("d64_q128_fp32", 1, 3, 1536, 64, "fp32", 128, 0.1, 0.7),
+    # fewer tokens than one block: one ragged query block and one ragged KV block
+    ("n1", 1, 2, 1, 64, "bf16", 64, 0.5, 0.9),
+    ("n37_fp32", 1, 2, 37, 128, "fp32", 128, 0.5, 0.9),
+    ("n65_q128", 2, 1, 65, 128, "bf16", 128, 0.3, 0.9),
 ]
 
 
@@ -278,6 +282,31 @@ def test_workload_output_sampled(name, per_head):
         want.append(ob)
     mx, rr = check_out(np.concatenate(got), np.concatenate(want), "bf16", name)
     log(f"{name}: sampled {len(rows)} rows max|dO| {mx:.2e} rel-RMS {rr:.2e}")
+
+
+def test_max_kv_blocks_sampled():
+    """The largest supported sequence: 4096 KV blocks (N = 262,144) in one head. Sampled
+    rows' masks bit-exact and their outputs within the bf16 bound."""
+    w = W.Workload("max_kv", 1, 1, 64, (64, 64, 64), "bf16", 128, 64, 0.01, 0.85, 16, seed=2)
+    assert w.n_kvblk == 4096
+    ent = inputs(w)
+    p, (rp, ci) = gpu_plan(w, ent)
+    rows = sample_rows(w, 8)
+    sub = oracle_plan(ent["q32"], ent["k32"], w.block_q, w.block_kv, w.topk, w.top_p, rows=rows)
+    for (b, h, I), kept in sub.items():
+        r = (b * w.H + h) * w.n_qblk + I
+        assert ci[rp[r]:rp[r + 1]].tolist() == kept.tolist(), (b, h, I)
+    o = sa.fwd(ent["dq"], ent["dk"], ent["dv"], p)
+    ref = sparse_attention(ent["q32"], ent["k32"], W.to_f32(ent["v"]), rp, ci, w.block_q, w.block_kv,
+                           rows=rows)
+    got, want = [], []
+    for (b, h, I), (ob, _) in ref.items():
+        sl = slice(I * w.block_q, min(w.N, (I + 1) * w.block_q))
+        got.append(to_f64(o[b, h, sl]))
+        want.append(ob)
+    mx, rr = check_out(np.concatenate(got), np.concatenate(want), "bf16", w.name)
+    log(f"{w.name}: nnz {rp[-1]}, sampled {len(rows)} rows max|dO| {mx:.2e} rel-RMS {rr:.2e}")
+    drop(w)
 
 
 @pytest.mark.parametrize("name,nrows", [("wan14b_720p", 24), ("long_245k", 8)])
