@@ -3,7 +3,7 @@
 One step = sparse_attn_plan (pool, scores, hybrid top-k/top-p select, CSR) followed by
 sparse_attn_fwd over the kept tiles, on seeded synthetic video-token Q, K, V already
 resident in HBM. By default the step goes through sparse_attn_pipelined, which runs the
-two over chunks of heads on two streams (--chunks, 4); the plain plan-then-forward
+two over chunks of heads on two streams (--chunks; by default 4 chunks on steps of at least 8192 query-block rows); the plain plan-then-forward
 sequence is timed as well (ms_step_sequential, ms_plan, ms_fwd). Prints one JSON line:
 
   value        effective TFLOP/s over the exact kept query-key pairs (4*D flops per
@@ -159,6 +159,9 @@ def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 15.0):
 
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+# Below this many query-block rows a quarter of the forward no longer fills the chip and
+# the pipelined step is slower than the plain sequence (480p: 0.75 against 0.59 ms).
+PIPE_MIN_ROWS = 8192
 
 
 def time_fp8(sa, torch, w, dq, dk, dv, p, flops, t_fwd_bf16, args, stream):
@@ -241,16 +244,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cubes", action="store_true",
-                    help="head-aware 3-D tiling: put each head's tokens in a cube order "
-                         "(per-head cubes cycled from a fixed list) before the plan and "
-                         "move the output back after the forward; both moves are timed")
+                    help="head-aware 3-D tiling: queries and keys taken per head in a cube "
+                         "order (per-head cubes cycled from a fixed list) through the plan's "
+                         "tables; nothing is moved")
     ap.add_argument("--quality", action="store_true",
                     help="also build the ground-truth tile heatmap of full attention (two "
                          "passes) and report the router mask's recall and retained mass")
-    ap.add_argument("--chunks", type=int, default=4,
+    ap.add_argument("--chunks", type=int, default=None,
                     help="heads per step are split into this many chunks, pipelined over two "
-                         "streams (plan of one chunk overlapping the forward of the previous); "
-                         "0 times the plain plan-then-forward sequence as the step")
+                         "streams (plans of later chunks under the forwards of earlier ones); "
+                         "0 times the plain plan-then-forward sequence as the step; default: 4 "
+                         "when the step has at least %d query-block rows, else 0" % PIPE_MIN_ROWS)
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward (dq, dk, dv) over the step's plan, from the "
                          "forward's o and lse and a synthetic upstream gradient")
@@ -282,27 +286,26 @@ def main():
     dalpha = dev(alpha) if w.linear else None
     stream = torch.cuda.current_stream()
     raw = (dq, dk, dv)
-    qc = kc = q_table = None
+    qc = kc = q_table = kv_table = None
     if args.cubes:
         # fixed per-head cubes (no search): t x h x w extents of 128 (query) and 64 (key).
-        # K and V are moved into cube order; q is read, and o written, in raster order
-        # through the plan's query-order table (built once, like the cube shapes).
+        # q, k and v stay in raster order; the forward reads them, and writes o, through
+        # the plan's query and key tables (built once, like the cube shapes).
         qc = [Q_CUBES[h % len(Q_CUBES)] for h in range(w.H)]
         kc = [KV_CUBES[h % len(KV_CUBES)] for h in range(w.H)]
         q_table = sa.cube_order(w.H, w.grid, qc)
-        dk, dv = torch.empty_like(dk), torch.empty_like(dv)
+        kv_table = sa.cube_order(w.H, w.grid, kc)
 
     def move_in():
-        if qc is not None:
-            sa.cube_permute(raw[1], w.grid, kc, out=dk)
-            sa.cube_permute(raw[2], w.grid, kc, out=dv)
+        pass
 
     def move_out():
         pass
 
     def make_plan():
         if q_table is not None:
-            return sa.plan_ordered(dq, dk, q_table, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+            return sa.plan_ordered(dq, dk, q_table, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws,
+                                   kv_order=kv_table)
         return sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
     ws = torch.empty(sa.plan_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv),
                      dtype=torch.uint8, device="cuda")
@@ -351,6 +354,8 @@ def main():
     log(f"step {t_step:.3f} ms (plan {t_plan:.3f}, fwd {t_fwd:.3f}); wall {1e3 * wall / args.steps:.3f} ms/step")
     t_seq = t_step
     ms_seq = ms_step
+    if args.chunks is None:
+        args.chunks = 4 if w.B * w.H * w.n_qblk >= PIPE_MIN_ROWS else 0
     pipelined = args.chunks > 0 and q_table is None and not w.linear
     if pipelined:
         # the step through the pipelined call: plan + forward over head chunks, two streams
@@ -426,7 +431,7 @@ def main():
             "pipeline": ({"chunks": args.chunks, "streams": 2, "call": "sparse_attn_pipelined"}
                          if pipelined else None),
             "cube_tiling": ({"query_cubes": Q_CUBES, "key_cubes": KV_CUBES, "per_head": "h mod 3",
-                             "moved": "k, v (q and o through the plan's query order)"}
+                             "moved": "nothing (q, k, v and o through the plan's tables)"}
                             if args.cubes else None),
         },
         "ms_step_sequential": round(t_seq, 4),
@@ -438,7 +443,6 @@ def main():
         "ms_plan_median": round(float(np.median(ms_plan)), 4),
         "ms_fwd_median": round(float(np.median(ms_fwd)), 4),
         "ms_fwd_min": round(float(np.min(ms_fwd)), 4),
-        **({"ms_cube_moves": round(float(np.mean(ms_move)), 4)} if args.cubes else {}),
         "fwd_tflops": round(achieved, 2),
         "kept_pairs": pairs,
         "nnz_tiles": nnz,
@@ -477,15 +481,17 @@ def main():
             raise SystemExit("--quality needs a bf16 workload")
         # the heatmap's query blocks must be the plan's rows: cube-ordered q under --cubes
         hq = sa.cube_permute(raw[0], w.grid, qc) if qc is not None else dq
+        hk = sa.cube_permute(raw[1], w.grid, kc) if qc is not None else dk
+        hv = sa.cube_permute(raw[2], w.grid, kc) if qc is not None else dv
         pd = sa.plan_dense(hq, w.block_q, w.block_kv)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        sa.fwd(hq, dk, dv, pd, return_lse=True, out=o, lse=lse)
-        tmax, tmass = sa.tile_stats(hq, dk, lse, w.block_q, w.block_kv)
+        sa.fwd(hq, hk, hv, pd, return_lse=True, out=o, lse=lse)
+        tmax, tmass = sa.tile_stats(hq, hk, lse, w.block_q, w.block_kv)
         e[0].record(stream)
-        sa.fwd(hq, dk, dv, pd, return_lse=True, out=o, lse=lse)
+        sa.fwd(hq, hk, hv, pd, return_lse=True, out=o, lse=lse)
         e[1].record(stream)
-        tmax, tmass = sa.tile_stats(hq, dk, lse, w.block_q, w.block_kv)
+        tmax, tmass = sa.tile_stats(hq, hk, lse, w.block_q, w.block_kv)
         e[2].record(stream)
         torch.cuda.synchronize()
         t2 = e[1].elapsed_time(e[2])
@@ -494,7 +500,7 @@ def main():
         qual["ms_pass2_tile_stats"] = round(t2, 3)
         qual["pass2_tflops"] = round(2.0 * w.D * w.B * w.H * float(w.N) * w.N / t2 / 1e9, 1)
         out["quality"] = qual
-        del pd, lse, tmax, tmass, hq
+        del pd, lse, tmax, tmass, hq, hk, hv
     if not args.no_cpu_baseline:
         if qc is not None:
             # the oracle on the same cube-ordered head 0 as the plan's CSR describes

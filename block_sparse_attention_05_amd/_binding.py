@@ -40,7 +40,7 @@ class SaPlan(ctypes.Structure):
         ("n_qblk", ctypes.c_int32), ("n_kvblk", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("row_order", ctypes.c_void_p),
-        ("q_order", ctypes.c_void_p),
+        ("q_order", ctypes.c_void_p), ("kv_order", ctypes.c_void_p),
     ]
 
 
@@ -68,7 +68,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_plan_workspace_bytes.restype = sz
     lib.sparse_attn_plan.argtypes = [vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, sz, pplan, vp]
     lib.sparse_attn_plan.restype = i32
-    lib.sparse_attn_plan_ordered.argtypes = [vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, vp, sz, pplan, vp]
+    lib.sparse_attn_plan_ordered.argtypes = [vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, vp, vp, sz, pplan, vp]
     lib.sparse_attn_plan_ordered.restype = i32
     lib.sparse_attn_plan_dense.argtypes = [i32] * 7 + [vp, sz, pplan, vp]
     lib.sparse_attn_plan_dense.restype = i32
@@ -232,18 +232,20 @@ def plan(q, k, block_q: int = 128, block_kv: int = 64, topk: float = 0.05, top_p
 
 
 def plan_ordered(q, k, q_order, block_q: int = 128, block_kv: int = 64, topk: float = 0.05,
-                 top_p: float = 0.9, stream=None, workspace=None) -> Plan:
+                 top_p: float = 0.9, stream=None, workspace=None, kv_order=None) -> Plan:
     """The mask for queries taken per head in the order q_order (int32 [H, N] GPU tensor,
-    position -> storage row; see sparse_attn_plan_ordered). q stays in storage order, k
-    (and the v later given to fwd) are in KV-block order; fwd with this plan writes o in
-    q's storage order."""
+    position -> storage row; see sparse_attn_plan_ordered) and, with kv_order, keys in
+    that order too. q (and k, v with kv_order) stay in storage order; without kv_order, k
+    and the v later given to fwd are in key-position order. fwd with this plan writes o
+    in q's storage order."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k)
     B, H, N, D = q.shape
-    if not (q_order.is_cuda and q_order.dtype == torch.int32 and q_order.is_contiguous()
-            and q_order.numel() == H * N):
-        raise ValueError("q_order must be a contiguous int32 [H, N] GPU tensor")
+    for t, name in ((q_order, "q_order"), (kv_order, "kv_order")):
+        if t is not None and not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()
+                                  and t.numel() == H * N):
+            raise ValueError(f"{name} must be a contiguous int32 [H, N] GPU tensor")
     need = lib.sparse_attn_plan_workspace_bytes(B, H, N, D, block_q, block_kv)
     if need == 0:
         raise SparseAttnError(SA_ERR_UNSUPPORTED, "plan shape")
@@ -251,9 +253,10 @@ def plan_ordered(q, k, q_order, block_q: int = 128, block_kv: int = 64, topk: fl
     st = SaPlan()
     _check(lib.sparse_attn_plan_ordered(q.data_ptr(), k.data_ptr(), _dtype_code(q), B, H, N, D,
                                         block_q, block_kv, float(topk), float(top_p),
-                                        q_order.data_ptr(), ws.data_ptr(), ws.numel(),
-                                        ctypes.byref(st), _stream(stream)), "sparse_attn_plan_ordered")
-    return Plan(ws, st, keep=q_order)
+                                        q_order.data_ptr(), kv_order.data_ptr() if kv_order is not None else None,
+                                        ws.data_ptr(), ws.numel(), ctypes.byref(st), _stream(stream)),
+           "sparse_attn_plan_ordered")
+    return Plan(ws, st, keep=(q_order, kv_order))
 
 
 def cube_order(H: int, grid, cubes, device="cuda", stream=None):

@@ -82,6 +82,7 @@ void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L
   p->col_idx = reinterpret_cast<int32_t *>(ws + L.col_idx);
   p->row_order = reinterpret_cast<int32_t *>(ws + L.row_order);
   p->q_order = nullptr;
+  p->kv_order = nullptr;
 }
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
@@ -127,8 +128,8 @@ size_t sparse_attn_plan_workspace_bytes(int B, int H, int N, int D, int block_q,
 namespace {
 sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, int N, int D,
                     int block_q, int block_kv, double topk_frac, double top_p,
-                    const int32_t *q_order, void *workspace, size_t ws_bytes, sa_plan *out,
-                    hipStream_t stream) {
+                    const int32_t *q_order, const int32_t *kv_order, void *workspace, size_t ws_bytes,
+                    sa_plan *out, hipStream_t stream) {
   if (q == nullptr || k == nullptr || out == nullptr) return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
   if (!(topk_frac >= 0.0 && topk_frac <= 1.0)) return SA_ERR_INVALID_ARG;
@@ -161,8 +162,9 @@ sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, 
   const int nwords = ceil_div(s.nKV, 32);
 
   p.q_order = q_order;
+  p.kv_order = kv_order;
   hipError_t e = launch_pool(q, dtype, BH, H, N, D, block_q, q_order, qbar, stream);
-  if (e == hipSuccess) e = launch_pool(k, dtype, BH, H, N, D, block_kv, nullptr, kbar, stream);
+  if (e == hipSuccess) e = launch_pool(k, dtype, BH, H, N, D, block_kv, kv_order, kbar, stream);
   if (e == hipSuccess) e = launch_scores(qbar, kbar, BH, s.nQ, s.nKV, D, c, scores, stream);
   if (e == hipSuccess)
     e = launch_select(scores, (int)s.R, s.nKV, m_k, p32, p_all, bitmap, nwords, counts, stream);
@@ -179,17 +181,17 @@ sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, 
 sa_status sparse_attn_plan(const void *q, const void *k, sa_dtype dtype, int B, int H, int N,
                            int D, int block_q, int block_kv, double topk_frac, double top_p,
                            void *workspace, size_t ws_bytes, sa_plan *out, hipStream_t stream) {
-  return plan_impl(q, k, dtype, B, H, N, D, block_q, block_kv, topk_frac, top_p, nullptr,
+  return plan_impl(q, k, dtype, B, H, N, D, block_q, block_kv, topk_frac, top_p, nullptr, nullptr,
                    workspace, ws_bytes, out, stream);
 }
 
 sa_status sparse_attn_plan_ordered(const void *q, const void *k, sa_dtype dtype, int B, int H,
                                    int N, int D, int block_q, int block_kv, double topk_frac,
-                                   double top_p, const int32_t *q_order, void *workspace,
-                                   size_t ws_bytes, sa_plan *out, hipStream_t stream) {
+                                   double top_p, const int32_t *q_order, const int32_t *kv_order,
+                                   void *workspace, size_t ws_bytes, sa_plan *out, hipStream_t stream) {
   if (q_order == nullptr) return SA_ERR_INVALID_ARG;
   if (dtype == SA_FP32) return SA_ERR_UNSUPPORTED;
-  return plan_impl(q, k, dtype, B, H, N, D, block_q, block_kv, topk_frac, top_p, q_order,
+  return plan_impl(q, k, dtype, B, H, N, D, block_q, block_kv, topk_frac, top_p, q_order, kv_order,
                    workspace, ws_bytes, out, stream);
 }
 
@@ -289,7 +291,9 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.col_idx = plan->col_idx;
   a.row_order = plan->row_order;
   a.q_order = plan->q_order;
-  if (a.q_order != nullptr && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  a.kv_order = plan->kv_order;
+  if ((a.q_order != nullptr || a.kv_order != nullptr) && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (a.kv_order != nullptr && alpha != nullptr) return SA_ERR_UNSUPPORTED;
   a.B = B;
   a.H = H;
   a.N = N;
@@ -398,7 +402,7 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
     const int hc = BH - c * L.per < L.per ? BH - c * L.per : L.per;
     char *ws = static_cast<char *>(workspace) + c * L.plan_bytes;
     st = plan_impl(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)), dtype, 1, hc,
-                   N, D, block_q, block_kv, topk_frac, top_p, nullptr, ws, L.plan_bytes, &plans[c],
+                   N, D, block_q, block_kv, topk_frac, top_p, nullptr, nullptr, ws, L.plan_bytes, &plans[c],
                    two ? aux_stream : stream);
     if (st == SA_OK && two && hipEventRecord(ev[c], aux_stream) != hipSuccess) st = SA_ERR_HIP;
   }
@@ -479,7 +483,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H,
       plan->n_kvblk != s.nKV)
     return SA_ERR_PLAN_MISMATCH;
   if (plan->row_ptr == nullptr || plan->col_idx == nullptr) return SA_ERR_INVALID_ARG;
-  if (plan->dtype != SA_BF16 || plan->q_order != nullptr) return SA_ERR_UNSUPPORTED;
+  if (plan->dtype != SA_BF16 || (plan->q_order != nullptr || plan->kv_order != nullptr)) return SA_ERR_UNSUPPORTED;
   const Fp8Layout L = fp8_layout(s);
   st = check_ws(pack, pack_bytes, L.total);
   if (st != SA_OK) return st;
@@ -552,7 +556,7 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
   if (plan->B != B || plan->H != H || plan->N != N || plan->D != D || plan->dtype != (int)dtype ||
       plan->row_ptr == nullptr || plan->col_idx == nullptr)
     return SA_ERR_PLAN_MISMATCH;
-  if (dtype != SA_BF16 || plan->q_order != nullptr) return SA_ERR_UNSUPPORTED;
+  if (dtype != SA_BF16 || (plan->q_order != nullptr || plan->kv_order != nullptr)) return SA_ERR_UNSUPPORTED;
   const BwdLayout L = bwd_layout(s);
   st = check_ws(workspace, ws_bytes, L.total);
   if (st != SA_OK) return st;

@@ -36,6 +36,7 @@ struct FwdArgs {
   float *lse;
   const int32_t *row_ptr, *col_idx, *row_order;
   const int32_t *q_order;  // NULL, or per head: query position -> storage row of q, o, lse
+  const int32_t *kv_order; // NULL, or per head: key position -> storage row of k, v
   int B, H, N, D, block_q, block_kv, n_qblk, n_kvblk;
   float scale_log2;        // log2(e) / sqrt(D)
   double scale_log2_f64;   // the same in fp64

@@ -62,7 +62,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int D, int NW, bool LIN>
+template <int D, int NW, bool LIN, bool GATHER>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = 64 * NW;
@@ -163,6 +163,36 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   }
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
   const int32_t *__restrict__ cols = a.col_idx + beg;
+
+  // Key positions through the plan's table (GATHER): key position p of this head is
+  // storage row kvo[p]. The tile's 64 rows come one per lane (tabv, lane r = row r); a
+  // direct-load lane takes its row's entry by a wave shuffle. Each lane offset above is
+  // row * 2D + column bytes, so the row part is swapped for the storage row.
+  const int32_t *kvo = GATHER ? a.kv_order + (size_t)(bh % a.H) * N : nullptr;
+  constexpr int RSH = D == 128 ? 8 : 7;   // log2(2D)
+  auto tab_load = [&](int J) { return min(max(kvo[min(J * kBk + lane, N - 1)], 0), N - 1); };
+  auto issue_g = [&](int tabv, char *kdst, char *vdst) {
+#pragma unroll
+    for (int m = 0; m < NIW; ++m) {
+      const int i = wid + m * NW;
+      if (i < NI) {
+        const int src = __shfl(tabv, (int)(goff[m] >> RSH));
+        const uint32_t off = ((uint32_t)src << RSH) + (goff[m] & ((1u << RSH) - 1));
+        __builtin_amdgcn_global_load_lds((gvoid_t *)(reinterpret_cast<const char *>(kg) + off),
+                                         (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VNIW; ++m) {
+      const int i = wid + m * NW;
+      if (i < VNI) {
+        const int src = __shfl(tabv, (int)(vgoff[m] >> RSH));
+        const uint32_t off = ((uint32_t)src << RSH) + (vgoff[m] & ((1u << RSH) - 1));
+        __builtin_amdgcn_global_load_lds((gvoid_t *)(reinterpret_cast<const char *>(vg) + off),
+                                         (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
+      }
+    }
+  };
 
   auto issue = [&](int J, char *kdst, char *vdst) {
     const int j0 = J * kBk;
@@ -311,17 +341,35 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // after it with the key mask.
   // The kept-block indices run one tile ahead of the loads that use them: the index of
   // tile it + 2 is fetched while tile it computes, so issuing a tile's loads never waits
-  // on a memory round trip.
+  // on a memory round trip. With GATHER the table entries of a tile are fetched one tile
+  // ahead of its loads and the indices one further.
   const int n = end - beg;
   const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
   int c_next = n > 1 ? cols[1] : 0;
-  issue(cols[0], k0s, v0s);
+  int tab_next = 0;
+  if constexpr (GATHER) {
+    issue_g(tab_load(__builtin_amdgcn_readfirstlane(cols[0])), k0s, v0s);
+    if (n > 1) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
+    c_next = n > 2 ? cols[2] : 0;
+  } else {
+    issue(cols[0], k0s, v0s);
+  }
+  // loads of tile t + 1 into (kd, vd), and the look-ahead for later tiles
+  auto next = [&](int t, char *kd, char *vd) {
+    if constexpr (GATHER) {
+      if (t + 1 < n) issue_g(tab_next, kd, vd);
+      if (t + 2 < n) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
+      if (t + 3 < n) c_next = cols[t + 3];
+    } else {
+      if (t + 1 < n) issue(__builtin_amdgcn_readfirstlane(c_next), kd, vd);
+      if (t + 2 < n) c_next = cols[t + 2];
+    }
+  };
   int it = 0;
   for (; it < n_full; it += 2) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 1 < n) issue(__builtin_amdgcn_readfirstlane(c_next), k1s, v1s);
-    if (it + 2 < n) c_next = cols[it + 2];
+    next(it, k1s, v1s);
     tile(cols[it], k0s, v0s, std::false_type{});
     if (it + 1 >= n_full) {
       ++it;
@@ -329,8 +377,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 2 < n) issue(__builtin_amdgcn_readfirstlane(c_next), k0s, v0s);
-    if (it + 3 < n) c_next = cols[it + 3];
+    next(it + 1, k0s, v0s);
     tile(cols[it + 1], k1s, v1s, std::false_type{});
   }
   if (n_full < n) {
@@ -372,13 +419,13 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool LIN>
+template <int D, bool LIN, bool GATHER>
 hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
   const int R = a.B * a.H * a.n_qblk;
   if (a.block_q == 128)
-    sparse_fwd_bf16_kernel<D, 4, LIN><<<R, 256, 0, s>>>(a);
+    sparse_fwd_bf16_kernel<D, 4, LIN, GATHER><<<R, 256, 0, s>>>(a);
   else
-    sparse_fwd_bf16_kernel<D, 2, LIN><<<R, 128, 0, s>>>(a);
+    sparse_fwd_bf16_kernel<D, 2, LIN, GATHER><<<R, 128, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -386,8 +433,10 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
   const bool lin = a.alpha != nullptr;
-  if (a.D == 128) return lin ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
-  return lin ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+  if (a.kv_order != nullptr)   // keys through the plan's table (no linear branch)
+    return a.D == 128 ? launch_d<128, false, true>(a, s) : launch_d<64, false, true>(a, s);
+  if (a.D == 128) return lin ? launch_d<128, true, false>(a, s) : launch_d<128, false, false>(a, s);
+  return lin ? launch_d<64, true, false>(a, s) : launch_d<64, false, false>(a, s);
 }
 
 }  // namespace sa

@@ -78,6 +78,9 @@ typedef struct sa_plan {
   const int32_t *q_order;    /* device [H*N] or NULL (caller-owned, see
                               * sparse_attn_plan_ordered): query position i of head h is
                               * raster token q_order[h*N + i] */
+  const int32_t *kv_order;   /* device [H*N] or NULL (caller-owned): key position j of head
+                              * h is raster token kv_order[h*N + j]; NULL: k and v are
+                              * already in key-position order */
 } sa_plan;
 
 /* Accepted shapes: D in {64, 128}; block_q in {64, 128}; block_kv = 64; B*H <= 65535;
@@ -120,18 +123,23 @@ sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, 
  * storage order (head-aware 3-D tiling, Veda page, section 2.2: query blocks that are
  * compact cubes of the token grid). q stays in storage (raster) order; query position i
  * of head h is token q_order[h*N + i], so query block I is positions [I*block_q, ...).
- * k is given already in the order whose consecutive blocks are the KV blocks (for
- * example moved by sparse_attn_cube_permute). The plan keeps the q_order pointer:
- * sparse_attn_fwd with this plan reads q through it and writes o (and lse) back to the
- * storage rows, so o needs no move back. v must be in k's order.
+ * Keys likewise: with kv_order, k (and the v later given to sparse_attn_fwd) stay in
+ * storage order and key position j of head h is token kv_order[h*N + j], so KV block J
+ * is positions [J*block_kv, ...); with kv_order NULL, k and v are given already in
+ * key-position order (for example moved by sparse_attn_cube_permute). The plan keeps
+ * both pointers: sparse_attn_fwd with this plan reads q, k and v through them and writes
+ * o (and lse) back to q's storage rows, so nothing is moved before or after.
  * q_order: device int32 [H*N], a permutation of 0..N-1 per head (sparse_attn_cube_order
- * builds one); it must outlive the plan's use. Entries outside [0, N) are clamped (the
- * results are then meaningless, but no access leaves the tensors). bf16 only (fp32:
- * SA_ERR_UNSUPPORTED). Otherwise as sparse_attn_plan. */
+ * builds one); kv_order: NULL or the same kind of table. Both must outlive the plan's
+ * use. Entries outside [0, N) are clamped (the results are then meaningless, but no
+ * access leaves the tensors). bf16 only (fp32: SA_ERR_UNSUPPORTED); sparse_attn_fwd
+ * with a kv_order plan has no linear branch (alpha: SA_ERR_UNSUPPORTED). Otherwise as
+ * sparse_attn_plan. */
 sa_status sparse_attn_plan_ordered(const void *q, const void *k, sa_dtype dtype, int B, int H,
                                    int N, int D, int block_q, int block_kv, double topk_frac,
-                                   double top_p, const int32_t *q_order, void *workspace,
-                                   size_t ws_bytes, sa_plan *out, hipStream_t stream);
+                                   double top_p, const int32_t *q_order,
+                                   const int32_t *kv_order, void *workspace, size_t ws_bytes,
+                                   sa_plan *out, hipStream_t stream);
 
 /* Workspace bytes sparse_attn_fwd needs: 0 without the linear branch. */
 size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_linear);

@@ -190,10 +190,21 @@ def test_plan_ordered_and_cube_order_validation(lib):
     st = B.SaPlan()
     shape = (1, 2, 1024, 64, 64, 64)
     f = lib.sparse_attn_plan_ordered
-    assert f(FAKE, FAKE, 0, *shape, 0.1, 0.9, None, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 1, *shape, 0.1, 0.9, FAKE, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_UNSUPPORTED
-    assert f(None, FAKE, 0, *shape, 0.1, 0.9, FAKE, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 0, *shape, 1.5, 0.9, FAKE, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+    for kvo in (None, FAKE):
+        assert f(FAKE, FAKE, 0, *shape, 0.1, 0.9, None, kvo, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+        assert f(FAKE, FAKE, 1, *shape, 0.1, 0.9, FAKE, kvo, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_UNSUPPORTED
+        assert f(None, FAKE, 0, *shape, 0.1, 0.9, FAKE, kvo, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+        assert f(FAKE, FAKE, 0, *shape, 1.5, 0.9, FAKE, kvo, FAKE, 1 << 40, ctypes.byref(st), None) == E.SA_ERR_INVALID_ARG
+    # a plan that reads keys through a table has no linear branch in the forward
+    pl = B.SaPlan()
+    pl.B, pl.H, pl.N, pl.D, pl.block_q, pl.block_kv = 1, 2, 1024, 64, 64, 64
+    pl.n_qblk, pl.n_kvblk, pl.dtype = 16, 16, 0
+    pl.row_ptr, pl.col_idx, pl.row_order, pl.q_order, pl.kv_order = FAKE, FAKE, FAKE, FAKE, FAKE
+    fw = lib.sparse_attn_fwd
+    assert fw(FAKE, FAKE, FAKE, 0, 1, 2, 1024, 64, ctypes.byref(pl), FAKE, FAKE, None, FAKE, 1 << 40,
+              None) == E.SA_ERR_UNSUPPORTED
+    assert fw(FAKE, FAKE, FAKE, 1, 1, 2, 1024, 64, ctypes.byref(pl), None, FAKE, None, None, 0,
+              None) == E.SA_ERR_PLAN_MISMATCH
     g = lib.sparse_attn_cube_order
     c = np.array([1, 4, 16, 2, 2, 2], dtype=np.int32)
     assert g(2, 4, 16, 16, None, FAKE, None) == E.SA_ERR_INVALID_ARG

@@ -152,3 +152,31 @@ def test_ordered_plan_equals_moved_queries(case):
     l2 = unpermute_heads(l2.cpu().numpy()[..., None], grid, qc)[..., 0]
     assert np.array_equal(l1.cpu().numpy(), l2)
     log(f"{name}: ordered path bitwise equal to the moved path (nnz {rp1[-1]})")
+
+
+@pytest.mark.parametrize("case", ORDERED, ids=[c[0] for c in ORDERED])
+def test_ordered_keys_through_table_equal_moved_keys(case):
+    """Keys and values read through the plan's key table (no moves at all) are bitwise the
+    same as moving k and v into cube order first: the same plan, o and lse. A plan with a
+    key table rejects the linear branch."""
+    name, H, D, grid, bq, topk, p, lin = case
+    w = W.Workload(name, 1, H, D, grid, "bf16", bq, 64, topk, p, 4, linear=lin, seed=3)
+    ent = inputs(w)
+    qc, kc = cubes_for(H, Q_CUBES), cubes_for(H, KV_CUBES)
+    qt = sa.cube_order(H, grid, qc)
+    kt = sa.cube_order(H, grid, kc)
+    kp = sa.cube_permute(ent["dk"], grid, kc)
+    vp = sa.cube_permute(ent["dv"], grid, kc)
+    p_tab = sa.plan_ordered(ent["dq"], ent["dk"], qt, bq, 64, topk, p, kv_order=kt)
+    p_mov = sa.plan_ordered(ent["dq"], kp, qt, bq, 64, topk, p)
+    rp1, ci1 = p_tab.csr()
+    rp2, ci2 = p_mov.csr()
+    assert np.array_equal(rp1, rp2) and np.array_equal(ci1, ci2)
+    o1, l1 = sa.fwd(ent["dq"], ent["dk"], ent["dv"], p_tab, return_lse=True)
+    o2, l2 = sa.fwd(ent["dq"], kp, vp, p_mov, return_lse=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    if lin:
+        with pytest.raises(sa.SparseAttnError):
+            sa.fwd(ent["dq"], ent["dk"], ent["dv"], p_tab, alpha=ent["dalpha"])
+    log(f"{name}: keys through the table bitwise equal to moved keys (nnz {rp1[-1]})")
