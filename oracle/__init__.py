@@ -26,8 +26,9 @@ Two tracks:
 * ``oracle.backward``: the gradients dQ, dK, dV of block-sparse attention in float64
   (the pages fine-tune through the sparse kernel).
 * ``oracle.fp8``: the low-bit forward (SLA2 page, quantisation-aware fine-tuning):
-  Q, K, V quantised to OCP FP8 E4M3 with power-of-two group scales, then attention in
-  float64 on the decoded values.
+  Q, K, V quantised to OCP FP8 E4M3 with power-of-two group scales (or Q and K to
+  symmetric int8 with fp32 group scales), then attention in float64 on the decoded
+  values.
 
 Parity pins (tests marked "not gpu") tie both tracks to facts outside the oracle:
 closed forms, library routines, brute force and hand-derived fixtures. Parity of the
@@ -42,7 +43,8 @@ from .heatmap import tile_heatmap
 from .tiling import cube_order, permute_heads, unpermute_heads
 from .backward import sparse_attention_backward
 from .fp8 import (e4m3_decode, e4m3_encode, scale_exponent, quantize_qkv, dequantize,
-                  fp8_attention)
+                  fp8_attention, int8_scales, int8_encode, quantize_qkv_i8qk, dequantize_i8qk,
+                  i8qk_attention)
 
 __all__ = [
     "exp_sa", "pool_blocks", "block_scores", "tree_sum", "select_row", "topk_count",
@@ -50,5 +52,6 @@ __all__ = [
     "sparse_attention", "dense_attention", "brute_masked_attention", "linear_branch",
     "blend", "phi", "dense_plan", "csr_to_mask", "tile_heatmap", "cube_order", "permute_heads",
     "unpermute_heads", "sparse_attention_backward", "e4m3_decode", "e4m3_encode",
-    "scale_exponent", "quantize_qkv", "dequantize", "fp8_attention",
+    "scale_exponent", "quantize_qkv", "dequantize", "fp8_attention", "int8_scales",
+    "int8_encode", "quantize_qkv_i8qk", "dequantize_i8qk", "i8qk_attention",
 ]

@@ -20,6 +20,14 @@ precision. The page names no format. The reading taken here:
 * Attention then runs in float64 on the decoded values code * 2^e
   (``oracle.attention.sparse_attention``): the quantisation is the definition of the
   low-bit forward, and everything after it is exact here.
+
+A second format keeps V as above and stores Q and K as symmetric 8-bit integers (the
+same groups), a more accurate choice for the logits on gfx950 at the same peak rate:
+for a group with largest magnitude a (an fp32 value), the inverse scale
+inv = fp32(127 / a) and the scale s = fp32(a / 127) are single fp32 divisions, a value
+x is stored as rint(fp32(x * inv)) (round half to even; it lies in [-127, 127]) and
+decodes to code * s. An all-zero group takes inv = s = 0. Every step is one IEEE fp32
+operation, so the codes are reproducible exactly.
 """
 from __future__ import annotations
 
@@ -128,4 +136,62 @@ def fp8_attention(q, k, v, row_ptr, col_idx, block_q: int, block_kv: int,
     float64 on the decoded values. Returns O [B, H, N, D] float64."""
     qc, qe, kc, ke, vc, ve = quantize_qkv(q, k, v, block_q, block_kv)
     qd, kd, vd = dequantize(qc, qe, kc, ke, vc, ve, block_q, block_kv)
+    return sparse_attention(qd, kd, vd, row_ptr, col_idx, block_q, block_kv, rows=rows)
+
+
+def int8_scales(amax):
+    """(inv, s) float32 for group maxima amax: inv = fp32(127 / a), s = fp32(a / 127);
+    0 and 0 for a zero group."""
+    a = np.asarray(amax, dtype=np.float32)
+    nz = a > 0
+    safe = np.where(nz, a, np.float32(1))
+    inv = np.where(nz, np.float32(127) / safe, np.float32(0)).astype(np.float32)
+    sc = np.where(nz, safe / np.float32(127), np.float32(0)).astype(np.float32)
+    return inv, sc
+
+
+def int8_encode(x, inv):
+    """rint(fp32(x * inv)) as int8, x and inv float32 (broadcast)."""
+    y = np.asarray(x, dtype=np.float32) * np.asarray(inv, dtype=np.float32)
+    return np.rint(y).astype(np.int8)
+
+
+def quantize_qkv_i8qk(q, k, v, block_q: int, block_kv: int):
+    """(qc, qs, kc, ks, vc, ve): Q and K as int8 codes [B, H, N, D] with fp32 scales per
+    query block [B, H, nQ] and per KV block [B, H, nKV]; V as quantize_qkv."""
+    q32, k32 = (np.asarray(t, dtype=np.float32) for t in (q, k))
+    B, H, N, D = q32.shape
+
+    def per_block(x, bs):
+        nb = -(-N // bs)
+        pad = nb * bs - N
+        ax = np.abs(x)
+        if pad:
+            ax = np.concatenate([ax, np.zeros((B, H, pad, D), np.float32)], axis=2)
+        amax = ax.reshape(B, H, nb, bs * D).max(axis=3)
+        inv, sc = int8_scales(amax)
+        codes = int8_encode(x, np.repeat(inv, bs, axis=2)[:, :, :N, None])
+        return codes, sc
+
+    qc, qs = per_block(q32, block_q)
+    kc, ks = per_block(k32, block_kv)
+    ve = scale_exponent(np.abs(np.asarray(v, np.float64)).max(axis=2))
+    vc = _quantize_groups(v, ve[:, :, None, :])
+    return qc, qs, kc, ks, vc, ve
+
+
+def dequantize_i8qk(qc, qs, kc, ks, vc, ve, block_q: int, block_kv: int):
+    """float64 q, k, v from the int8-QK format (exact)."""
+    N = qc.shape[2]
+    q = qc.astype(np.float64) * np.repeat(qs.astype(np.float64), block_q, axis=2)[:, :, :N, None]
+    k = kc.astype(np.float64) * np.repeat(ks.astype(np.float64), block_kv, axis=2)[:, :, :N, None]
+    v = np.ldexp(e4m3_decode(vc), ve[:, :, None, :])
+    return q, k, v
+
+
+def i8qk_attention(q, k, v, row_ptr, col_idx, block_q: int, block_kv: int, rows=None):
+    """The low-bit forward with int8 Q and K: quantise as above, then block-sparse
+    attention in float64 on the decoded values."""
+    parts = quantize_qkv_i8qk(q, k, v, block_q, block_kv)
+    qd, kd, vd = dequantize_i8qk(*parts, block_q, block_kv)
     return sparse_attention(qd, kd, vd, row_ptr, col_idx, block_q, block_kv, rows=rows)

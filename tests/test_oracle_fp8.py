@@ -159,3 +159,69 @@ def test_p_rounding_model_below_gpu_bounds():
     mx = np.abs(oh - o).max() / np.abs(vd).max()
     assert rr < 0.5e-2 and mx < 0.015, (rr, mx)
     assert rr > 1e-4                                  # the rounding does act
+
+
+# ------------------------------------------------------------------ int8 Q and K
+from oracle.fp8 import (dequantize_i8qk, i8qk_attention, int8_encode, int8_scales,  # noqa: E402
+                        quantize_qkv_i8qk)
+
+
+def test_int8_scales_are_correctly_rounded_divisions():
+    """fp32 a / 127 and 127 / a: a quotient of two fp32 values computed in fp64 and rounded
+    once to fp32 is the correctly rounded fp32 quotient (53 >= 2*24 + 2)."""
+    rng = np.random.default_rng(11)
+    a = np.concatenate([np.exp(rng.uniform(-20, 20, 5000)), [1.0, 127.0, 254.0, 3.0e-30]]).astype(np.float32)
+    inv, sc = int8_scales(a)
+    assert np.array_equal(sc, (a.astype(np.float64) / 127.0).astype(np.float32))
+    assert np.array_equal(inv, (127.0 / a.astype(np.float64)).astype(np.float32))
+    z_inv, z_sc = int8_scales(np.zeros(3, np.float32))
+    assert not z_inv.any() and not z_sc.any()
+
+
+def test_int8_encode_is_nearest_with_ties_to_even():
+    rng = np.random.default_rng(12)
+    y = np.concatenate([rng.uniform(-127, 127, 4000), np.arange(-127, 127) + 0.5]).astype(np.float32)
+    got = int8_encode(y, np.float32(1)).astype(np.int64)
+    cand = np.arange(-127, 128)
+    d = np.abs(y.astype(np.float64)[:, None] - cand[None, :])
+    best = d.min(axis=1, keepdims=True)
+    ties = (d == best)
+    # nearest; on a tie the even candidate
+    want = np.array([c[t][np.argmax(c[t] % 2 == 0)] if t.sum() > 1 else c[t][0]
+                     for c, t in zip(np.broadcast_to(cand, d.shape), ties)])
+    assert np.array_equal(got, want)
+
+
+def test_int8_qk_bounds_and_group_max():
+    rng = np.random.default_rng(13)
+    B, H, N, D = 1, 2, 200, 64
+    q, k, v = (rng.normal(size=(B, H, N, D)).astype(np.float32) * s for s in (1.0, 3.0, 0.5))
+    qc, qs, kc, ks, vc, ve = quantize_qkv_i8qk(q, k, v, 64, 64)
+    assert qc.dtype == np.int8 and np.abs(qc.astype(int)).max() <= 127
+    qd, kd, _ = dequantize_i8qk(qc, qs, kc, ks, vc, ve, 64, 64)
+    for x, xd, sc in ((q, qd, np.repeat(qs, 64, axis=2)[:, :, :N, None]),
+                      (k, kd, np.repeat(ks, 64, axis=2)[:, :, :N, None])):
+        bound = sc.astype(np.float64) / 2 + np.abs(x) * 2.0 ** -22
+        assert np.all(np.abs(xd - x) <= bound)
+    for blk in range(-(-N // 64)):
+        assert np.all(np.abs(qc[:, :, blk * 64:(blk + 1) * 64].astype(int)).max(axis=(2, 3)) == 127)
+
+
+def test_int8_qk_identity_case():
+    """Integer-valued q and k whose groups reach 127 quantise to themselves (scale 1), and
+    the forward equals float64 attention on them."""
+    rng = np.random.default_rng(14)
+    B, H, N, D, bq, bk = 1, 1, 192, 64, 64, 64
+    q = rng.integers(-127, 128, size=(B, H, N, D)).astype(np.float32)
+    k = rng.integers(-127, 128, size=(B, H, N, D)).astype(np.float32)
+    q[:, :, ::64, 0] = 127
+    k[:, :, ::64, 0] = -127
+    v = rng.normal(size=(B, H, N, D))
+    qc, qs, kc, ks, vc, ve = quantize_qkv_i8qk(q, k, v, bq, bk)
+    assert (qs == 1).all() and (ks == 1).all()
+    assert np.array_equal(qc.astype(np.float32), q) and np.array_equal(kc.astype(np.float32), k)
+    rp, ci = dense_plan(B, H, N, bq, bk)
+    _, _, vd = dequantize_i8qk(qc, qs, kc, ks, vc, ve, bq, bk)
+    ref = sparse_attention(q.astype(np.float64) / 16, k.astype(np.float64) / 16, vd, rp, ci, bq, bk)
+    got = i8qk_attention(q / 16, k / 16, v, rp, ci, bq, bk)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
