@@ -158,46 +158,52 @@ def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 15.0):
     }
 
 
-PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (int8: 5.0 POP/s, the same rate)
 # Below this many query-block rows a quarter of the forward no longer fills the chip and
 # the pipelined step is slower than the plain sequence (480p: 0.75 against 0.59 ms).
 PIPE_MIN_ROWS = 8192
 
 
 def time_fp8(sa, torch, w, dq, dk, dv, p, flops, t_fwd_bf16, args, stream):
-    """Times the low-bit forward over the plan p: the quantiser (Q, K, V to the FP8 pack)
-    and the fp8 attention kernel, each with HIP events on the launch stream."""
-    pack = sa.quantize_fp8(dq, dk, dv, w.block_q)
+    """Times the low-bit forward over the plan p for both q/k formats (E4M3, int8; v is
+    E4M3 in both): the quantiser and the attention kernel, each with HIP events on the
+    launch stream."""
+    out = {"format": "v: OCP FP8 E4M3, power-of-two scale per channel; q, k: E4M3 with a "
+                     "power-of-two scale per block (e4m3) or int8 with an fp32 scale per block (int8)"}
     o = torch.empty_like(dq)
-    for _ in range(max(1, args.warmup)):
-        sa.quantize_fp8(dq, dk, dv, w.block_q, out=pack)
-        sa.fwd_fp8(pack, p, out=o)
-    n = max(3, args.steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
-    torch.cuda.synchronize()
-    for i in range(n):
-        ev[i][0].record(stream)
-        sa.quantize_fp8(dq, dk, dv, w.block_q, out=pack)
-        ev[i][1].record(stream)
-        sa.fwd_fp8(pack, p, out=o)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    tq = [e[0].elapsed_time(e[1]) for e in ev]
-    tf = [e[1].elapsed_time(e[2]) for e in ev]
-    t = float(np.mean(tf))
-    log(f"fp8: quantise {np.mean(tq):.3f} ms, forward {t:.3f} ms (bf16 forward {t_fwd_bf16:.3f} ms)")
     qkv_bytes = 3.0 * w.B * w.H * w.N * w.D * 2
-    return {
-        "ms_quantize": round(float(np.mean(tq)), 4),
-        "ms_fwd_fp8": round(t, 4),
-        "ms_fwd_fp8_median": round(float(np.median(tf)), 4),
-        "ms_fwd_fp8_min": round(float(np.min(tf)), 4),
-        "fwd_fp8_tflops": round(flops / t / 1e9, 2),
-        "fwd_fp8_frac_of_fp8_peak": round(flops / t / 1e9 / PEAK_FP8_TFLOPS, 4),
-        "speedup_fwd_vs_bf16": round(t_fwd_bf16 / t, 3),
-        "quantize_gbs": round(qkv_bytes * 1.5 / (float(np.mean(tq)) * 1e-3) / 1e9, 1),
-        "format": "OCP FP8 E4M3, power-of-two scales: q per query block, k per 64-key block, v per channel",
-    }
+    for qk in ("e4m3", "int8"):
+        pack = sa.quantize_fp8(dq, dk, dv, w.block_q, qk=qk)
+        for _ in range(max(1, args.warmup)):
+            sa.quantize_fp8(dq, dk, dv, w.block_q, out=pack, qk=qk)
+            sa.fwd_fp8(pack, p, out=o)
+        n = max(3, args.steps)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record(stream)
+            sa.quantize_fp8(dq, dk, dv, w.block_q, out=pack, qk=qk)
+            ev[i][1].record(stream)
+            sa.fwd_fp8(pack, p, out=o)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        tq = [e[0].elapsed_time(e[1]) for e in ev]
+        tf = [e[1].elapsed_time(e[2]) for e in ev]
+        t = float(np.mean(tf))
+        log(f"low-bit ({qk} q, k): quantise {np.mean(tq):.3f} ms, forward {t:.3f} ms "
+            f"(bf16 forward {t_fwd_bf16:.3f} ms)")
+        out[qk] = {
+            "ms_quantize": round(float(np.mean(tq)), 4),
+            "ms_fwd": round(t, 4),
+            "ms_fwd_median": round(float(np.median(tf)), 4),
+            "ms_fwd_min": round(float(np.min(tf)), 4),
+            "fwd_tflops": round(flops / t / 1e9, 2),
+            "fwd_frac_of_fp8_int8_peak": round(flops / t / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "speedup_fwd_vs_bf16": round(t_fwd_bf16 / t, 3),
+            "quantize_gbs": round(qkv_bytes * 1.5 / (float(np.mean(tq)) * 1e-3) / 1e9, 1),
+        }
+        del pack
+    return out
 
 
 def time_backward(sa, torch, w, dq, dk, dv, p, pairs, args, stream):
@@ -259,8 +265,8 @@ def main():
                     help="also time the backward (dq, dk, dv) over the step's plan, from the "
                          "forward's o and lse and a synthetic upstream gradient")
     ap.add_argument("--fp8", action="store_true",
-                    help="also time the low-bit forward over the step's plan: the FP8 quantiser "
-                         "and the fp8-MFMA attention kernel")
+                    help="also time the low-bit forward over the step's plan, q and k in E4M3 and in "
+                         "int8: the quantiser and the attention kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

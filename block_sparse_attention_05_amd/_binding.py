@@ -95,9 +95,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_pipelined.restype = i32
     lib.sparse_attn_fp8_pack_bytes.argtypes = [i32] * 6
     lib.sparse_attn_fp8_pack_bytes.restype = sz
-    lib.sparse_attn_quantize_fp8.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [vp, sz, vp]
+    lib.sparse_attn_quantize_fp8.argtypes = [vp, vp, vp, i32] + [i32] * 7 + [vp, sz, vp]
     lib.sparse_attn_quantize_fp8.restype = i32
-    lib.sparse_attn_fwd_fp8.argtypes = [vp, sz, i32, i32, i32, i32, pplan, vp, vp, vp]
+    lib.sparse_attn_fwd_fp8.argtypes = [vp, sz, i32, i32, i32, i32, i32, pplan, vp, vp, vp]
     lib.sparse_attn_fwd_fp8.restype = i32
     lib.sparse_attn_router_exp.argtypes = [vp, vp, i64, vp]
     lib.sparse_attn_router_exp.restype = i32
@@ -371,11 +371,12 @@ class Fp8Pack:
     """FP8 E4M3 codes and group exponents of q, k, v in one device buffer (layout as
     documented for sparse_attn_fp8_pack_bytes)."""
 
-    def __init__(self, buf, shape, block_q: int, block_kv: int):
+    def __init__(self, buf, shape, block_q: int, block_kv: int, qk: str = "e4m3"):
         self.buf = buf
         self.shape = tuple(shape)
         self.block_q = block_q
         self.block_kv = block_kv
+        self.qk = qk          # "e4m3" or "int8": the format of the q and k codes
 
     def _parts(self):
         B, H, N, D = self.shape
@@ -398,7 +399,10 @@ class Fp8Pack:
         raw = self.buf[off:off + n]
         shapes = {"q8": (B, H, N, D), "k8": (B, H, N, D), "vt8": (B, H, nKV, D, 64),
                   "qe": (B, H, nQ), "ke": (B, H, nKV), "ve": (B, H, D), "vamax": (B, H, D)}
-        t = raw if name in ("q8", "k8", "vt8") else raw.view(torch.int32)
+        if name in ("q8", "k8", "vt8"):
+            t = raw.view(torch.int8) if (self.qk == "int8" and name != "vt8") else raw
+        else:
+            t = raw.view(torch.float32 if (self.qk == "int8" and name in ("qe", "ke")) else torch.int32)
         return t.view(shapes[name])
 
 
@@ -406,21 +410,28 @@ def fp8_pack_bytes(B, H, N, D, block_q=128, block_kv=64) -> int:
     return int(load_library().sparse_attn_fp8_pack_bytes(B, H, N, D, block_q, block_kv))
 
 
+QK_FORMATS = {"e4m3": 0, "int8": 1}
+
+
 def quantize_fp8(q, k, v, block_q: int = 128, block_kv: int = 64, out: Optional[Fp8Pack] = None,
-                 stream=None) -> Fp8Pack:
-    """Quantises bf16 q, k, v [B, H, N, D] to an FP8 pack (see sparse_attn_quantize_fp8)."""
+                 stream=None, qk: str = "e4m3") -> Fp8Pack:
+    """Quantises bf16 q, k, v [B, H, N, D] to a low-bit pack (see sparse_attn_quantize_fp8):
+    v always E4M3; q and k E4M3 (qk="e4m3") or int8 (qk="int8")."""
+    if qk not in QK_FORMATS:
+        raise ValueError("qk must be 'e4m3' or 'int8'")
     lib = load_library()
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
     need = lib.sparse_attn_fp8_pack_bytes(B, H, N, D, block_q, block_kv)
     if need == 0:
         raise SparseAttnError(SA_ERR_UNSUPPORTED, "fp8 pack shape")
-    pack = out if out is not None else Fp8Pack(_new_ws(need, q.device), q.shape, block_q, block_kv)
+    pack = out if out is not None else Fp8Pack(_new_ws(need, q.device), q.shape, block_q, block_kv, qk)
     if pack.shape != tuple(q.shape) or pack.block_q != block_q:
         raise ValueError("pack was made for another shape or block_q")
+    pack.qk = qk
     _check(lib.sparse_attn_quantize_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, N, D,
-                                        block_q, block_kv, pack.buf.data_ptr(), pack.buf.numel(),
-                                        _stream(stream)), "sparse_attn_quantize_fp8")
+                                        block_q, block_kv, QK_FORMATS[qk], pack.buf.data_ptr(),
+                                        pack.buf.numel(), _stream(stream)), "sparse_attn_quantize_fp8")
     return pack
 
 
@@ -438,7 +449,8 @@ def fwd_fp8(pack: Fp8Pack, plan: Plan, return_lse: bool = False, out=None, lse=N
         raise ValueError("o must be a contiguous bf16 [B, H, N, D] tensor")
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    _check(lib.sparse_attn_fwd_fp8(pack.buf.data_ptr(), pack.buf.numel(), B, H, N, D, ctypes.byref(plan.st),
+    _check(lib.sparse_attn_fwd_fp8(pack.buf.data_ptr(), pack.buf.numel(), QK_FORMATS[pack.qk], B, H, N, D,
+                                   ctypes.byref(plan.st),
                                    o.data_ptr(), lse.data_ptr() if return_lse else None, _stream(stream)),
            "sparse_attn_fwd_fp8")
     return (o, lse) if return_lse else o

@@ -453,9 +453,10 @@ size_t sparse_attn_fp8_pack_bytes(int B, int H, int N, int D, int block_q, int b
 }
 
 sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, sa_dtype dtype, int B, int H,
-                                   int N, int D, int block_q, int block_kv, void *pack, size_t pack_bytes,
-                                   hipStream_t stream) {
+                                   int N, int D, int block_q, int block_kv, int qk_format, void *pack,
+                                   size_t pack_bytes, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr) return SA_ERR_INVALID_ARG;
+  if (qk_format != SA_QK_E4M3 && qk_format != SA_QK_INT8) return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
   Shape s;
   sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
@@ -470,12 +471,14 @@ sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, 
             reinterpret_cast<int32_t *>(pk + L.ke),   reinterpret_cast<int32_t *>(pk + L.ve),
             reinterpret_cast<uint32_t *>(pk + L.vamax)};
   return hip_status(launch_quantize_fp8(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                                        static_cast<const uint16_t *>(v), B * H, N, D, s.bq, p, stream));
+                                        static_cast<const uint16_t *>(v), B * H, N, D, s.bq,
+                                        qk_format == SA_QK_INT8, p, stream));
 }
 
-sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H, int N, int D,
+sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format, int B, int H, int N, int D,
                               const sa_plan *plan, void *o, float *lse, hipStream_t stream) {
   if (pack == nullptr || plan == nullptr || o == nullptr) return SA_ERR_INVALID_ARG;
+  if (qk_format != SA_QK_E4M3 && qk_format != SA_QK_INT8) return SA_ERR_INVALID_ARG;
   Shape s;
   sa_status st = check_shape(B, H, N, D, plan->block_q, plan->block_kv, &s);
   if (st != SA_OK) return st;
@@ -508,7 +511,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H,
   a.n_qblk = s.nQ;
   a.n_kvblk = s.nKV;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-  return hip_status(launch_fwd_fp8(a, stream));
+  return hip_status(launch_fwd_fp8(a, qk_format == SA_QK_INT8, stream));
 }
 
 namespace {

@@ -40,6 +40,8 @@ namespace sa {
 namespace {
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -87,9 +89,19 @@ __device__ __forceinline__ float block_max_256(float v, float *red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// One workgroup per (block of BLK rows, head): the block's max |x|, its exponent, and the
-// codes of its rows. grid (ceil(N / BLK), B*H), 256 threads.
-template <int D, int BLK>
+// four values -> four int8 codes rint(x * inv) in one dword (byte u = value u)
+__device__ __forceinline__ uint32_t to_i8x4(float a, float b, float c, float d, float inv) {
+  const int ca = (int)rintf(__fmul_rn(a, inv)), cb = (int)rintf(__fmul_rn(b, inv));
+  const int cc = (int)rintf(__fmul_rn(c, inv)), cd = (int)rintf(__fmul_rn(d, inv));
+  return (uint32_t)(ca & 0xFF) | ((uint32_t)(cb & 0xFF) << 8) | ((uint32_t)(cc & 0xFF) << 16) |
+         ((uint32_t)(cd & 0xFF) << 24);
+}
+
+// One workgroup per (block of BLK rows, head): the block's max |x|, its exponent (E4M3)
+// or fp32 scale (I8), and the codes of its rows. grid (ceil(N / BLK), B*H), 256 threads.
+// I8: inv = 127 / a and s = a / 127 (correctly rounded fp32 divisions), code =
+// rint(x * inv); an all-zero block takes inv = s = 0.
+template <int D, int BLK, bool I8>
 __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t *__restrict__ x, int N, int nblk,
                                                              uint8_t *__restrict__ out, int32_t *__restrict__ exps) {
   constexpr int GPR = D / 8;                 // 16-byte granules per row
@@ -111,20 +123,37 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t *__r
 #pragma unroll
     for (int u = 0; u < 4; ++u) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[u])), fabsf(bf16_hi(w[u]))));
   }
-  const int ex = fp8_exponent(block_max_256(amax, red));
-  if (threadIdx.x == 0) exps[(size_t)bh * nblk + blk] = ex;
+  const float bmax = block_max_256(amax, red);
   uint2 *dst = reinterpret_cast<uint2 *>(out + base);
+  if constexpr (I8) {
+    const float inv = bmax > 0.f ? __fdiv_rn(127.0f, bmax) : 0.0f;
+    if (threadIdx.x == 0) exps[(size_t)bh * nblk + blk] = __float_as_int(bmax > 0.f ? __fdiv_rn(bmax, 127.0f) : 0.0f);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + i * 256;
-    if (e < ng) {
-      const uint32_t w[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
-      uint2 r;
-      r.x = to_fp8x4(ldexpf(bf16_lo(w[0]), -ex), ldexpf(bf16_hi(w[0]), -ex), ldexpf(bf16_lo(w[1]), -ex),
-                     ldexpf(bf16_hi(w[1]), -ex));
-      r.y = to_fp8x4(ldexpf(bf16_lo(w[2]), -ex), ldexpf(bf16_hi(w[2]), -ex), ldexpf(bf16_lo(w[3]), -ex),
-                     ldexpf(bf16_hi(w[3]), -ex));
-      dst[e] = r;
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * 256;
+      if (e < ng) {
+        const uint32_t w[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+        uint2 r;
+        r.x = to_i8x4(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]), inv);
+        r.y = to_i8x4(bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3]), inv);
+        dst[e] = r;
+      }
+    }
+  } else {
+    const int ex = fp8_exponent(bmax);
+    if (threadIdx.x == 0) exps[(size_t)bh * nblk + blk] = ex;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * 256;
+      if (e < ng) {
+        const uint32_t w[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+        uint2 r;
+        r.x = to_fp8x4(ldexpf(bf16_lo(w[0]), -ex), ldexpf(bf16_hi(w[0]), -ex), ldexpf(bf16_lo(w[1]), -ex),
+                       ldexpf(bf16_hi(w[1]), -ex));
+        r.y = to_fp8x4(ldexpf(bf16_lo(w[2]), -ex), ldexpf(bf16_hi(w[2]), -ex), ldexpf(bf16_lo(w[3]), -ex),
+                       ldexpf(bf16_hi(w[3]), -ex));
+        dst[e] = r;
+      }
     }
   }
 }
@@ -230,7 +259,7 @@ __device__ __forceinline__ int swz(int r) {
   return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
-template <int D, int NW>
+template <int D, int NW, bool I8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
   constexpr int BQ = 32 * NW;
@@ -278,18 +307,30 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
     return;
   }
 
-  // Q fragments (B operand of S^T = K Q^T): channels m*64 + hf*32 + 0..31
+  // Q fragments (B operand of S^T = K Q^T). E4M3: channels m*64 + hf*32 + 0..31 for the
+  // 32x32x64 MFMA; I8: channels m*32 + hf*16 + 0..15 for v_mfma_i32_32x32x32_i8.
   intx8 qf[MS];
+  intx4 qf4[DT];
+  if constexpr (I8) {
 #pragma unroll
-  for (int m = 0; m < MS; ++m) {
-    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-    if (q_ok) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(qg + (size_t)qi * D + m * 64 + hf * 32);
-      w0 = p[0];
-      w1 = p[1];
+    for (int m = 0; m < DT; ++m) {
+      uint4 w0 = make_uint4(0, 0, 0, 0);
+      if (q_ok) w0 = *reinterpret_cast<const uint4 *>(qg + (size_t)qi * D + m * 32 + hf * 16);
+      qf4[m] = intx4{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
     }
-    qf[m] = intx8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+  } else {
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+      uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+      if (q_ok) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(qg + (size_t)qi * D + m * 64 + hf * 32);
+        w0 = p[0];
+        w1 = p[1];
+      }
+      qf[m] = intx8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+    }
   }
+  // E4M3: the block's exponent; I8: its fp32 scale (bits)
   const int eq = a.qe[(size_t)bh * nQ + I];
   const int32_t *__restrict__ keb = a.ke + (size_t)bh * a.n_kvblk;
 
@@ -349,6 +390,9 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
   for (int m = 0; m < MS; ++m)
 #pragma unroll
     for (int s = 0; s < 2; ++s) kro[m][s] = l32 * D + (((m * 4 + hf * 2 + s) ^ swz<D>(l32)) * 16);
+  int kro4[DT];   // I8: granule m*2 + hf
+#pragma unroll
+  for (int m = 0; m < DT; ++m) kro4[m] = l32 * D + (((m * 2 + hf) ^ swz<D>(l32)) * 16);
   int vro[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) vro[s] = l32 * 64 + (((hf * 2 + s) ^ swz<64>(l32)) * 16);
@@ -374,19 +418,42 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
 
   auto tile = [&](int J, int ek, const char *kt_s, const char *vt_s, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const float mul = ldexpf(sl2, eq + ek);
     floatx16 sacc[2];
+    float mul;
+    if constexpr (I8) {
+      // exact int32 dot products of the codes, then one fp32 multiplier: sq * sk * log2(e)/sqrt(D)
+      mul = sl2 * __int_as_float(eq) * __int_as_float(ek);
+      intx16 iacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) iacc[kt][i] = 0;
 #pragma unroll
-    for (int m = 0; m < MS; ++m)
+      for (int m = 0; m < DT; ++m)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const intx8 kf = ld8(kt_s + kt * 32 * D, kro[m][0], kro[m][1]);
-        sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[m], sacc[kt], 0, 0, 0, 0, 0, 0);
-      }
+        for (int kt = 0; kt < 2; ++kt) {
+          const uint4 x = *reinterpret_cast<const uint4 *>(kt_s + kt * 32 * D + kro4[m]);
+          iacc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(intx4{(int)x.x, (int)x.y, (int)x.z, (int)x.w}, qf4[m],
+                                                           iacc[kt], 0, 0, 0);
+        }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = (float)iacc[kt][i];
+    } else {
+      mul = ldexpf(sl2, eq + ek);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < MS; ++m)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const intx8 kf = ld8(kt_s + kt * 32 * D, kro[m][0], kro[m][1]);
+          sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[m], sacc[kt], 0, 0, 0, 0, 0, 0);
+        }
+    }
     if constexpr (MASK) {
       const int valid = N - J * kBk;
 #pragma unroll
@@ -511,27 +578,27 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool I8>
 hipError_t launch_fwd_fp8_d(const Fp8FwdArgs &a, hipStream_t s) {
   const int R = a.B * a.H * a.n_qblk;
   if (a.block_q == 128)
-    sparse_fwd_fp8_kernel<D, 4><<<R, 256, 0, s>>>(a);
+    sparse_fwd_fp8_kernel<D, 4, I8><<<R, 256, 0, s>>>(a);
   else
-    sparse_fwd_fp8_kernel<D, 2><<<R, 128, 0, s>>>(a);
+    sparse_fwd_fp8_kernel<D, 2, I8><<<R, 128, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool I8>
 hipError_t launch_quant_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, int BH, int N, int bq,
                           const Fp8Pack &p, hipStream_t s) {
   const int nQ = ceil_div(N, bq), nKV = ceil_div(N, kBk);
   fill_u32_kernel<<<ceil_div(BH * D, 256), 256, 0, s>>>(p.vamax, BH * D);
   fp8_vamax_kernel<D><<<dim3(ceil_div(N, kVChunk), BH), 256, 0, s>>>(v, N, p.vamax);
   if (bq == 128)
-    fp8_quant_rows_kernel<D, 128><<<dim3(nQ, BH), 256, 0, s>>>(q, N, nQ, p.q8, p.qe);
+    fp8_quant_rows_kernel<D, 128, I8><<<dim3(nQ, BH), 256, 0, s>>>(q, N, nQ, p.q8, p.qe);
   else
-    fp8_quant_rows_kernel<D, 64><<<dim3(nQ, BH), 256, 0, s>>>(q, N, nQ, p.q8, p.qe);
-  fp8_quant_rows_kernel<D, 64><<<dim3(nKV, BH), 256, 0, s>>>(k, N, nKV, p.k8, p.ke);
+    fp8_quant_rows_kernel<D, 64, I8><<<dim3(nQ, BH), 256, 0, s>>>(q, N, nQ, p.q8, p.qe);
+  fp8_quant_rows_kernel<D, 64, I8><<<dim3(nKV, BH), 256, 0, s>>>(k, N, nKV, p.k8, p.ke);
   fp8_quant_vt_kernel<D><<<dim3(nKV, BH), 2 * D, 0, s>>>(v, N, nKV, p.vamax, p.vt8, p.ve);
   return hipGetLastError();
 }
@@ -539,12 +606,15 @@ hipError_t launch_quant_d(const uint16_t *q, const uint16_t *k, const uint16_t *
 }  // namespace
 
 hipError_t launch_quantize_fp8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int BH, int N, int D,
-                               int bq, const Fp8Pack &p, hipStream_t s) {
-  return D == 128 ? launch_quant_d<128>(q, k, v, BH, N, bq, p, s) : launch_quant_d<64>(q, k, v, BH, N, bq, p, s);
+                               int bq, int i8qk, const Fp8Pack &p, hipStream_t s) {
+  if (i8qk)
+    return D == 128 ? launch_quant_d<128, true>(q, k, v, BH, N, bq, p, s) : launch_quant_d<64, true>(q, k, v, BH, N, bq, p, s);
+  return D == 128 ? launch_quant_d<128, false>(q, k, v, BH, N, bq, p, s) : launch_quant_d<64, false>(q, k, v, BH, N, bq, p, s);
 }
 
-hipError_t launch_fwd_fp8(const Fp8FwdArgs &a, hipStream_t s) {
-  return a.D == 128 ? launch_fwd_fp8_d<128>(a, s) : launch_fwd_fp8_d<64>(a, s);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs &a, int i8qk, hipStream_t s) {
+  if (i8qk) return a.D == 128 ? launch_fwd_fp8_d<128, true>(a, s) : launch_fwd_fp8_d<64, true>(a, s);
+  return a.D == 128 ? launch_fwd_fp8_d<128, false>(a, s) : launch_fwd_fp8_d<64, false>(a, s);
 }
 
 }  // namespace sa

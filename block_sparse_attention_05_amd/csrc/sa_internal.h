@@ -98,8 +98,9 @@ struct Fp8Pack {
   int32_t *qe, *ke, *ve;    // [B,H,nQ], [B,H,nKV], [B,H,D]
   uint32_t *vamax;          // [B,H,D] scratch
 };
+// i8qk: Q and K as int8 codes with fp32 scales (in qe, ke) instead of E4M3 with exponents
 hipError_t launch_quantize_fp8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int BH, int N, int D,
-                               int bq, const Fp8Pack &p, hipStream_t s);
+                               int bq, int i8qk, const Fp8Pack &p, hipStream_t s);
 struct Fp8FwdArgs {
   const uint8_t *q8, *k8, *vt8;
   const int32_t *qe, *ke, *ve;
@@ -109,7 +110,7 @@ struct Fp8FwdArgs {
   int B, H, N, D, block_q, n_qblk, n_kvblk;
   float scale_log2;         // log2(e) / sqrt(D)
 };
-hipError_t launch_fwd_fp8(const Fp8FwdArgs &a, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs &a, int i8qk, hipStream_t s);
 // Tile heatmap, pass 2 (heatmap.hip): per (row, KV block) max and mean mass of exp(s - lse).
 hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
                              int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s);

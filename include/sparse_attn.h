@@ -208,19 +208,28 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
  * (batch, head, query block of block_q tokens), k per (batch, head, 64-key block), v per
  * (batch, head, channel) over all tokens.
  *
+ * A second format (qk_format = SA_QK_INT8) keeps v as above and stores q and k as
+ * symmetric int8 codes, more accurate on the logits at the same MFMA rate: for a group
+ * with largest magnitude a, inv = 127 / a and s = a / 127 (correctly rounded fp32
+ * divisions; 0 and 0 for an all-zero group), and x is stored as rint(fp32(x * inv)),
+ * ties to even, decoding to code * s.
+ *
  * The pack is one device buffer of sparse_attn_fp8_pack_bytes bytes holding, each part
  * starting at the next 256-byte boundary after the previous one, in this order:
- *   q8     uint8 [B, H, N, D]       codes of q, row-major;
- *   k8     uint8 [B, H, N, D]       codes of k;
+ *   q8     uint8 [B, H, N, D]       codes of q, row-major (int8 codes with SA_QK_INT8);
+ *   k8     uint8 [B, H, N, D]       codes of k (likewise);
  *   vt8    uint8 [B, H, nKV, D, 64] codes of v, each 64-key block transposed to channel
  *                                   rows; byte h*32 + b (h in {0, 1}, b < 32) of a row
  *                                   holds key (b/16)*32 + ((b/4)%4)*8 + h*4 + b%4 of the
  *                                   block; keys past N hold 0;
  *   qe     int32 [B, H, nQ]         exponents of the q groups (nQ = ceil(N/block_q));
- *   ke     int32 [B, H, nKV]        exponents of the k groups (nKV = ceil(N/64));
+ *                                   with SA_QK_INT8 the fp32 scales s, as bit patterns;
+ *   ke     int32 [B, H, nKV]        exponents of the k groups (nKV = ceil(N/64)); likewise;
  *   ve     int32 [B, H, D]          exponents of the v groups;
  *   vamax  uint32 [B, H, D]         the quantiser's scratch (per-channel max |v|). */
 size_t sparse_attn_fp8_pack_bytes(int B, int H, int N, int D, int block_q, int block_kv);
+
+typedef enum { SA_QK_E4M3 = 0, SA_QK_INT8 = 1 } sa_qk_format;
 
 /* Quantises q, k, v (device [B, H, N, D] bf16, finite) into pack (device, 256-byte
  * aligned, pack_bytes >= sparse_attn_fp8_pack_bytes). block_q must be the block_q of the
@@ -228,17 +237,20 @@ size_t sparse_attn_fp8_pack_bytes(int B, int H, int N, int D, int block_q, int b
  * Deterministic. */
 sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, sa_dtype dtype,
                                    int B, int H, int N, int D, int block_q, int block_kv,
-                                   void *pack, size_t pack_bytes, hipStream_t stream);
+                                   int qk_format, void *pack, size_t pack_bytes,
+                                   hipStream_t stream);
 
 /* Block-sparse attention over the plan's kept tiles computed from an FP8 pack: the
  * products q k^T and P v run on fp8 MFMA with fp32 accumulation, the softmax in fp32,
  * and P (the probabilities scaled by 2^8 against the running maximum) is rounded to
  * E4M3 before it multiplies v; the row sums add the same rounded values.
- * pack: as sparse_attn_quantize_fp8 wrote it, with the plan's block_q.
+ * pack: as sparse_attn_quantize_fp8 wrote it, with the plan's block_q and the same
+ * qk_format (SA_QK_INT8: q k^T on int8 MFMA with exact int32 sums, scaled in fp32).
  * plan: a bf16 plan for [B, H, N, D] without a query order (else SA_ERR_UNSUPPORTED).
  * o: device [B, H, N, D] bf16. lse: device float [B, H, N] or NULL, as sparse_attn_fwd. */
-sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int B, int H, int N, int D,
-                              const sa_plan *plan, void *o, float *lse, hipStream_t stream);
+sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format, int B, int H,
+                              int N, int D, const sa_plan *plan, void *o, float *lse,
+                              hipStream_t stream);
 
 /* Ground-truth tile heatmap of full attention (Veda page, section 2.1: the reference mask
  * max-pools the full attention matrix over query x key tiles; section 2.3: two passes).

@@ -269,9 +269,10 @@ def test_fp8_quantize_and_fwd_validation(lib):
     q = lib.sparse_attn_quantize_fp8
 
     def quant(**kw):
-        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, shape=(1, 2, 1024, 64), bq=64, bk=64, pack=FAKE, pb=need)
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, shape=(1, 2, 1024, 64), bq=64, bk=64, fmt=0, pack=FAKE, pb=need)
         a.update(kw)
-        return q(a["q"], a["k"], a["v"], a["dt"], *a["shape"], a["bq"], a["bk"], a["pack"], a["pb"], None)
+        return q(a["q"], a["k"], a["v"], a["dt"], *a["shape"], a["bq"], a["bk"], a["fmt"], a["pack"], a["pb"],
+                 None)
 
     for name in ("q", "k", "v"):
         assert quant(**{name: None}) == B.SA_ERR_INVALID_ARG, name
@@ -282,6 +283,8 @@ def test_fp8_quantize_and_fwd_validation(lib):
     assert quant(pack=FAKE + 16) == B.SA_ERR_WORKSPACE
     assert quant(bk=128) == B.SA_ERR_UNSUPPORTED
     assert quant(shape=(1, 2, 1024, 80)) == B.SA_ERR_UNSUPPORTED
+    assert quant(fmt=2) == B.SA_ERR_INVALID_ARG
+    assert quant(fmt=-1) == B.SA_ERR_INVALID_ARG
 
     st = B.SaPlan()
     st.B, st.H, st.N, st.D, st.block_q, st.block_kv = 1, 2, 1024, 64, 64, 64
@@ -290,11 +293,12 @@ def test_fp8_quantize_and_fwd_validation(lib):
     f = lib.sparse_attn_fwd_fp8
 
     def fwd(**kw):
-        a = dict(pack=FAKE, pb=need, shape=(1, 2, 1024, 64), o=FAKE, lse=None)
+        a = dict(pack=FAKE, pb=need, fmt=0, shape=(1, 2, 1024, 64), o=FAKE, lse=None)
         a.update(kw)
-        return f(a["pack"], a["pb"], *a["shape"], ctypes.byref(st), a["o"], a["lse"], None)
+        return f(a["pack"], a["pb"], a["fmt"], *a["shape"], ctypes.byref(st), a["o"], a["lse"], None)
 
     assert fwd(pack=None) == B.SA_ERR_INVALID_ARG
+    assert fwd(fmt=3) == B.SA_ERR_INVALID_ARG
     assert fwd(o=None) == B.SA_ERR_INVALID_ARG
     assert fwd(pb=need - 1) == B.SA_ERR_WORKSPACE
     assert fwd(shape=(1, 2, 2048, 64)) == B.SA_ERR_PLAN_MISMATCH

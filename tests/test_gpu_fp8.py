@@ -22,7 +22,7 @@ import torch
 import block_sparse_attention_05_amd as sa
 import workloads as W
 from oracle import sparse_attention
-from oracle.fp8 import dequantize, quantize_qkv
+from oracle.fp8 import dequantize, dequantize_i8qk, quantize_qkv, quantize_qkv_i8qk
 from tests.gpu_common import inputs, log, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -63,19 +63,37 @@ def _case(case):
     return w, inputs(w)
 
 
+def _oracle_codes(ent, w, qk):
+    v32 = W.to_f32(ent["v"])
+    if qk == "int8":
+        return quantize_qkv_i8qk(ent["q32"], ent["k32"], v32, w.block_q, 64)
+    return quantize_qkv(ent["q32"], ent["k32"], v32, w.block_q, 64)
+
+
+def _oracle_decoded(ent, w, qk):
+    parts = _oracle_codes(ent, w, qk)
+    return (dequantize_i8qk if qk == "int8" else dequantize)(*parts, w.block_q, 64)
+
+
+QK = ["e4m3", "int8"]
+
+
+@pytest.mark.parametrize("qk", QK)
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_quantize_bitexact(case):
+def test_quantize_bitexact(case, qk):
     w, ent = _case(case)
-    pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q)
+    pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q, qk=qk)
     torch.cuda.synchronize()
-    qc, qe, kc, ke, vc, ve = quantize_qkv(ent["q32"], ent["k32"], W.to_f32(ent["v"]), w.block_q, 64)
-    assert np.array_equal(pack.part("qe").cpu().numpy(), qe)
-    assert np.array_equal(pack.part("ke").cpu().numpy(), ke)
+    qc, qe, kc, ke, vc, ve = _oracle_codes(ent, w, qk)
+    bits = (lambda t: t.cpu().numpy().view(np.int32)) if qk == "int8" else (lambda t: t.cpu().numpy())
+    ref_bits = (lambda a: np.asarray(a, np.float32).view(np.int32)) if qk == "int8" else (lambda a: a)
+    assert np.array_equal(bits(pack.part("qe")), ref_bits(qe))
+    assert np.array_equal(bits(pack.part("ke")), ref_bits(ke))
     assert np.array_equal(pack.part("ve").cpu().numpy(), ve)
     assert np.array_equal(pack.part("q8").cpu().numpy(), qc)
     assert np.array_equal(pack.part("k8").cpu().numpy(), kc)
     assert np.array_equal(unpack_vt(pack.part("vt8").cpu().numpy(), w.N), vc)
-    log(f"{case[0]}: codes and exponents bit-exact (q exps {qe.min()}..{qe.max()}, v exps {ve.min()}..{ve.max()})")
+    log(f"{case[0]} {qk}: codes and scales bit-exact (v exps {ve.min()}..{ve.max()})")
 
 
 def _check(o, ref, vmax, what):
@@ -88,22 +106,23 @@ def _check(o, ref, vmax, what):
     return rr, mx
 
 
+@pytest.mark.parametrize("qk", QK)
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_fwd_fp8_parity(case):
+def test_fwd_fp8_parity(case, qk):
     w, ent = _case(case)
     plan = sa.plan(ent["dq"], ent["dk"], w.block_q, 64, w.topk, w.top_p)
-    pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q)
+    pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q, qk=qk)
     o, lse = sa.fwd_fp8(pack, plan, return_lse=True)
     rp, ci = plan.csr()
     v32 = W.to_f32(ent["v"])
-    qd, kd, vd = dequantize(*quantize_qkv(ent["q32"], ent["k32"], v32, w.block_q, 64), w.block_q, 64)
+    qd, kd, vd = _oracle_decoded(ent, w, qk)
     ref, ref_lse = sparse_attention(qd, kd, vd, rp, ci, w.block_q, 64, with_lse=True)
     rr, mx = _check(to_f64(o), ref, float(np.abs(vd).max()), case[0])
     dl = np.abs(lse.cpu().numpy() - ref_lse)
     assert float(dl.max()) <= TOL_LSE, f"lse: max {dl.max():.3e}"
     exact = sparse_attention(ent["q32"], ent["k32"], v32, rp, ci, w.block_q, 64)
     e = to_f64(o) - exact
-    log(f"{case[0]}: nnz {rp[-1]}; vs the low-bit oracle rel-RMS {rr:.2e}, max {mx:.2e}, lse max {dl.max():.2e}; "
+    log(f"{case[0]} {qk}: nnz {rp[-1]}; vs the low-bit oracle rel-RMS {rr:.2e}, max {mx:.2e}, lse max {dl.max():.2e}; "
         f"vs exact attention on the bf16 inputs rel-RMS {np.sqrt((e ** 2).sum() / (exact ** 2).sum()):.2e}")
 
 
@@ -137,26 +156,28 @@ def test_fwd_fp8_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_fp8_480p_sampled():
+@pytest.mark.parametrize("qk", QK)
+def test_fp8_480p_sampled(qk):
     """The 480p workload: codes of sampled heads bit-exact, outputs of sampled query
     blocks against the oracle."""
     from tests.gpu_common import sample_rows
     w = W.CONFIGS["wan13b_480p"]
     ent = inputs(w)
     plan = sa.plan(ent["dq"], ent["dk"], w.block_q, w.block_kv, w.topk, w.top_p)
-    pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q)
+    pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q, qk=qk)
     o = sa.fwd_fp8(pack, plan)
     rp, ci = plan.csr()
     heads = [(0, 0), (0, w.H - 1)]
     hs = [h for _, h in heads]
     v32 = W.to_f32(ent["v"])
     sub = lambda x: x[:, hs]
-    qc, qe, kc, ke, vc, ve = quantize_qkv(sub(ent["q32"]), sub(ent["k32"]), sub(v32), w.block_q, 64)
+    quant = quantize_qkv_i8qk if qk == "int8" else quantize_qkv
+    qc, qe, kc, ke, vc, ve = quant(sub(ent["q32"]), sub(ent["k32"]), sub(v32), w.block_q, 64)
     assert np.array_equal(pack.part("q8")[:, hs].cpu().numpy(), qc)
     assert np.array_equal(pack.part("k8")[:, hs].cpu().numpy(), kc)
     assert np.array_equal(unpack_vt(pack.part("vt8")[:, hs].cpu().numpy(), w.N), vc)
     assert np.array_equal(pack.part("ve")[:, hs].cpu().numpy(), ve)
-    qd, kd, vd = dequantize(qc, qe, kc, ke, vc, ve, w.block_q, 64)
+    qd, kd, vd = (dequantize_i8qk if qk == "int8" else dequantize)(qc, qe, kc, ke, vc, ve, w.block_q, 64)
     rows = [r for r in sample_rows(w, 6, heads=heads)]
     # the oracle on the two heads: rows re-indexed to the two-head sub-problem
     nq = w.n_qblk
@@ -175,4 +196,4 @@ def test_fp8_480p_sampled():
         g.append(got[b, hi, I * w.block_q:min(w.N, (I + 1) * w.block_q)])
         r.append(ob)
     rr, mx = _check(np.concatenate(g), np.concatenate(r), float(np.abs(vd).max()), "480p")
-    log(f"480p fp8 sampled ({len(rows)} query blocks): rel-RMS {rr:.2e}, max {mx:.2e}")
+    log(f"480p {qk} sampled ({len(rows)} query blocks): rel-RMS {rr:.2e}, max {mx:.2e}")
