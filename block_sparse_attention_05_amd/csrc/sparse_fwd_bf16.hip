@@ -6,12 +6,17 @@
 //   S^T = K Q^T      bf16 MFMA 32x32x16; each lane holds the 32 scores of one query for
 //                    its half of the tile, so max and sum are in-lane plus one exchange
 //                    between the two lane halves;
-//   softmax          log2 domain, fp32, raw v_exp_f32. The O rescale (which touches
-//                    every accumulator) runs only when some lane's running max grows; a
-//                    lazier max (rescaling only past a margin) is not used, because it
-//                    leaves the dominant key's probability off 1.0, and rounding that
-//                    probability to bf16 then shows up at full weight in outputs that
-//                    one key dominates;
+//   softmax          log2 domain, fp32, raw v_exp_f32. The row sums add the bf16-rounded
+//                    probabilities that the MFMA multiplies. Without an LSE output the
+//                    running max is lazy: it moves only when a tile's max passes it by
+//                    more than kLazy (log2 units), so the O rescale (which touches every
+//                    accumulator) runs on few tiles, and probabilities stay below
+//                    2^kLazy, which bf16 holds at the same relative precision. A dominant
+//                    key's probability is then no longer exactly 1, but its rounding
+//                    cancels in O = sum(p v) / sum(p). It does not cancel in the sum
+//                    itself (up to 2^-8 relative, the bf16 unit roundoff), so when the
+//                    LSE is written the max is exact (margin 0) and the largest term of
+//                    every row sum is exactly 1;
 //   O^T += V^T P^T   bf16 MFMA; P packed with v_cvt_pk_bf16_f32.
 // K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4), row-major with
 // one pad granule per row, double-buffered: the next tile's loads are in flight while the
@@ -44,6 +49,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lbf16x4_t;
 constexpr int kVmcnt0 = 0x0F70;
 
 constexpr int kBk = 64;            // keys per tile
+constexpr float kLazy = 8.0f;      // lazy-max margin, log2 units
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   const int q = G / 8;
@@ -246,6 +252,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running max, scaled logits, log2 domain
   float lsum[2] = {0.0f, 0.0f};  // this lane's part of the running sum (two chains)
   const float sl2 = a.scale_log2;
+  const float lazy = a.lse ? 0.0f : kLazy;
 
   // per-lane LDS byte offsets. K operand: row l32, granule hf. V^T operand source: row
   // hf*4 + u/4 and channel 32t + 16*(group & 1) + 4*(u & 3) (u = lane & 15), whose 64-byte
@@ -292,10 +299,10 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mt = mx * sl2;
-    const bool need = mt > m_run;
+    const bool need = mt > m_run + lazy;
     if (__ballot(need)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = need ? mt : m_run;
+      const float corr = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
       lsum[0] *= corr;
       lsum[1] *= corr;
 #pragma unroll

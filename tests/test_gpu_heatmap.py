@@ -8,8 +8,11 @@ Tolerances, derived from the arithmetic:
   is a few fp32 ulps of |s*c| (at most about 1e-3 for the sink-scaled keys here), so p
   is within a relative 2e-3 (plus 1e-6 absolute for tiny values).
 * End to end (log-sum-exp from the bf16 forward on the all-ones plan): that forward sums
-  the probabilities as rounded to bf16, each within 2^-9 relative, so its sum and hence
-  every p is within a further relative 2e-3: 5e-3 in all.
+  the probabilities as rounded to bf16, each within 2^-8 relative (the bf16 unit
+  roundoff). When it writes the log-sum-exp its running max is exact, so the largest
+  term of every sum is exactly 1 and the others' roundings are independent; the sum's
+  relative error stays well below 2^-8, and the bar takes a further relative 3e-3 for
+  it: 5e-3 in all.
 """
 import numpy as np
 import pytest
