@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import List, Optional, Tuple
 
 import numpy as np
 
@@ -40,7 +40,7 @@ class SaPlan(ctypes.Structure):
         ("n_qblk", ctypes.c_int32), ("n_kvblk", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("row_order", ctypes.c_void_p),
-        ("q_order", ctypes.c_void_p), ("kv_order", ctypes.c_void_p),
+        ("q_order", ctypes.c_void_p), ("kv_order", ctypes.c_void_p), ("visit", ctypes.c_void_p),
     ]
 
 
@@ -196,6 +196,16 @@ class Plan:
         rp = self.row_ptr().cpu().numpy().astype(np.int64)
         ci = self.col_idx(int(rp[-1])).cpu().numpy()
         return rp, ci
+
+    def visit_lists(self) -> Optional[List[np.ndarray]]:
+        """Each row's kept blocks in the forward's visit order (host arrays; synchronises),
+        or None when the plan has no visit lists."""
+        if not self.st.visit:
+            return None
+        rp = self.row_ptr().cpu().numpy().astype(np.int64)
+        nkv = self.st.n_kvblk
+        full = self._view(self.st.visit, self.rows * nkv).view(self.rows, nkv).cpu().numpy()
+        return [full[r, :rp[r + 1] - rp[r]].copy() for r in range(self.rows)]
 
 
 def _new_ws(nbytes: int, device):

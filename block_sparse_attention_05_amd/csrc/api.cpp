@@ -83,6 +83,7 @@ void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L
   p->row_order = reinterpret_cast<int32_t *>(ws + L.row_order);
   p->q_order = nullptr;
   p->kv_order = nullptr;
+  p->visit = nullptr;
 }
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
@@ -163,11 +164,13 @@ sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, 
 
   p.q_order = q_order;
   p.kv_order = kv_order;
+  p.visit = reinterpret_cast<int32_t *>(scores);   // the select kernel's visit lists
   hipError_t e = launch_pool(q, dtype, BH, H, N, D, block_q, q_order, qbar, stream);
   if (e == hipSuccess) e = launch_pool(k, dtype, BH, H, N, D, block_kv, kv_order, kbar, stream);
   if (e == hipSuccess) e = launch_scores(qbar, kbar, BH, s.nQ, s.nKV, D, c, scores, stream);
   if (e == hipSuccess)
-    e = launch_select(scores, (int)s.R, s.nKV, m_k, p32, p_all, bitmap, nwords, counts, stream);
+    e = launch_select(scores, (int)s.R, s.nKV, N % block_kv != 0, m_k, p32, p_all, bitmap, nwords, counts,
+                      stream);
   if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, stream);
   if (e == hipSuccess) e = launch_fill(bitmap, nwords, p.row_ptr, (int)s.R, p.col_idx, stream);
   if (e == hipSuccess)
@@ -290,6 +293,7 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.row_ptr = plan->row_ptr;
   a.col_idx = plan->col_idx;
   a.row_order = plan->row_order;
+  a.visit = plan->visit;
   a.q_order = plan->q_order;
   a.kv_order = plan->kv_order;
   if ((a.q_order != nullptr || a.kv_order != nullptr) && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
@@ -503,6 +507,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format
   a.row_ptr = plan->row_ptr;
   a.col_idx = plan->col_idx;
   a.row_order = plan->row_order;
+  a.visit = plan->visit;
   a.B = B;
   a.H = H;
   a.N = N;

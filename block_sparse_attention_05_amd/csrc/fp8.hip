@@ -20,7 +20,12 @@
 //   S^T = K Q^T        D/64 MFMAs per 32-key half; the tile's scale 2^(eq + ek) joins
 //                      log2(e)/sqrt(D) in one multiplier per tile;
 //   P                  exp2 in fp32, offset by 2^8 so that P * 256 in [0, 256] uses the
-//                      E4M3 range, packed to fp8 with v_cvt_pk_fp8_f32;
+//                      E4M3 range, packed to fp8 with v_cvt_pk_fp8_f32. Without an LSE
+//                      output the running max is lazy: it moves only when a tile's max
+//                      passes it by more than kLazy (log2 units), P is offset by
+//                      2^(8 - kLazy) to stay within 256, and the O rescale runs on few
+//                      tiles. With the LSE the max is exact, so that the largest term of
+//                      each row sum is exactly 2^8 (lazily, it would carry E4M3 rounding);
 //   row sums           one MFMA of an all-ones A operand against P: the sums of exactly
 //                      the rounded probabilities the PV product multiplies, off the VALU;
 //   O^T += V^T P^T     D/32 MFMAs per tile; the per-channel V scale 2^ev is applied once
@@ -48,6 +53,7 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 
 constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt: all vector-memory operations done
 constexpr int kExpMin = -64, kExpMax = 64;
+constexpr float kLazy = 4.0f;     // lazy-max margin (log2 units) without an LSE output
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   const int q = G / 8;
@@ -347,7 +353,7 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
     voffs[m] = vr * 64 + ((vp ^ swz<64>(vr)) * 16);
   }
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
-  const int32_t *__restrict__ cols = a.col_idx + beg;
+  const int32_t *__restrict__ cols = a.visit ? a.visit + (size_t)row * a.n_kvblk : a.col_idx + beg;
 
   auto issue = [&](int J, char *kdst, char *vdst) {
     const uint8_t *kb = kg + (size_t)J * kBk * D;
@@ -409,6 +415,8 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
   float m_run = -INFINITY;  // running max of the scaled logits, log2 domain
   const float sl2 = a.scale_log2;
+  const float lazy = a.lse ? 0.0f : kLazy;
+  const float poff = 8.0f - lazy;   // P is stored times 2^poff: at most 2^8
 
   auto ld8 = [](const char *p0, int o0, int o1) {
     const uint4 x = *reinterpret_cast<const uint4 *>(p0 + o0);
@@ -471,10 +479,10 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mt = mx * mul;
-    const bool need = mt > m_run;
+    const bool need = mt > m_run + lazy;
     if (__ballot(need)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = need ? mt : m_run;
+      const float corr = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) lacc[i] *= corr;
 #pragma unroll
@@ -483,8 +491,8 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
         for (int i = 0; i < 16; ++i) oacc[t][i] *= corr;
       m_run = m_new;
     }
-    // P * 2^8 = exp2(s * mul - m_run + 8), in [0, 256]
-    const float msub = m_run - 8.0f;
+    // P * 2^poff = exp2(s * mul - m_run + poff), in [0, 256]
+    const float msub = m_run - poff;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -574,7 +582,7 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
         pk.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
         *reinterpret_cast<uint2 *>(orow + d) = pk;
       }
-    if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot) - 8.0f) * 0.69314718055994531f;
+    if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot) - poff) * 0.69314718055994531f;
   }
 }
 

@@ -269,8 +269,15 @@ constexpr int kCandCap = 512;   // largest candidate set ranked without the full
 // running sum over at most kCandCap terms) contains the top-p crossing. Its blocks are
 // ranked by counting, then scanned exactly as the full sort would be. Rows whose set is
 // larger than kCandCap take the full bitonic sort.
+//
+// The kept blocks also leave the kernel in score order (descending, ties to the lower
+// index), the order in which the forward kernels visit them: the row's slots of S are
+// read once at the start, so their first `count` entries are then overwritten with the
+// block indices (int32). A ragged last block, when kept, is moved to the end of the list,
+// so only a row's last tile ever carries the key mask. The forward's running max then
+// settles on the first tiles, and few later tiles rescale the output.
 template <int ITEMS>
-__global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S, int nKV,
+__global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragged_last,
                                                      int m_k, float p, int p_all,
                                                      uint32_t *__restrict__ bitmap,
                                                      int nwords, int32_t *__restrict__ counts) {
@@ -284,12 +291,28 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
   __shared__ int hist[128];
   __shared__ unsigned long long hmass[128];   // per-bin sum of e in 2^-40 fixed point
   __shared__ float red[4];
-  __shared__ int sh_count, sh_ncand, sh_bstar, sh_pos;
+  __shared__ int sh_count, sh_ncand, sh_bstar, sh_pos, sh_rag;
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const float *s = S + (size_t)row * nKV;
+  float *ord = S + (size_t)row * nKV;   // takes int32 block indices (bit patterns)
+
+  // list[0, count): kept keys in score order -> ord, ragged block last. Called after a
+  // barrier that follows the last read of s.
+  auto write_order = [&](const uint64_t *list, int count) {
+    if (tid == 0) sh_rag = -1;
+    __syncthreads();
+    if (ragged_last)
+      for (int r = tid; r < count; r += 256)
+        if ((int)(uint32_t)list[r] == nKV - 1) sh_rag = r;
+    __syncthreads();
+    const int rag = sh_rag;
+    for (int r = tid; r < count; r += 256)
+      if (r != rag) ord[r - (rag >= 0 && r > rag ? 1 : 0)] = __int_as_float((int)(uint32_t)list[r]);
+    if (rag >= 0 && tid == 0) ord[count - 1] = __int_as_float(nKV - 1);
+  };
 
   float sv[ITEMS];
 #pragma unroll
@@ -341,11 +364,12 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
   const float thr = p * z;
 
   if (p_all || m_k >= nKV) {
-    // every block is kept
+    // every block is kept (visited in index order; the ragged block is last anyway)
     for (int w = tid; w < nwords; w += 256) {
       const int rem = nKV - 32 * w;
       bitmap[(size_t)row * nwords + w] = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
     }
+    for (int J = tid; J < nKV; J += 256) ord[J] = __int_as_float(J);
     if (tid == 0) counts[row] = nKV;
     return;
   }
@@ -455,6 +479,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
       __syncthreads();
       for (int w = tid; w < nwords; w += 256) bitmap[(size_t)row * nwords + w] = bits[w];
       if (tid == 0) counts[row] = count;
+      write_order(csort, count);
       return;
     }
   }
@@ -531,6 +556,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ S
   __syncthreads();
   for (int w = tid; w < nwords; w += 256) bitmap[(size_t)row * nwords + w] = bits[w];
   if (tid == 0) counts[row] = count;
+  write_order(keys, count);
 }
 
 // ---------------------------------------------------------------- CSR
@@ -759,18 +785,21 @@ hipError_t launch_scores(const float *qbar, const float *kbar, int BH, int nQ, i
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float *scores, int R, int nKV, int m_k, float p, int p_all,
+hipError_t launch_select(float *scores, int R, int nKV, int ragged_last, int m_k, float p, int p_all,
                          uint32_t *bitmap, int nwords, int32_t *counts, hipStream_t s) {
+#define SA_SELECT(IT) \
+  select_kernel<IT><<<R, 256, 0, s>>>(scores, nKV, ragged_last, m_k, p, p_all, bitmap, nwords, counts)
   if (nKV <= 256)
-    select_kernel<1><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+    SA_SELECT(1);
   else if (nKV <= 512)
-    select_kernel<2><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+    SA_SELECT(2);
   else if (nKV <= 1024)
-    select_kernel<4><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+    SA_SELECT(4);
   else if (nKV <= 2048)
-    select_kernel<8><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+    SA_SELECT(8);
   else
-    select_kernel<16><<<R, 256, 0, s>>>(scores, nKV, m_k, p, p_all, bitmap, nwords, counts);
+    SA_SELECT(16);
+#undef SA_SELECT
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@ hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int H, int N, int D, 
                        const int32_t *order, float *out, hipStream_t s);
 hipError_t launch_scores(const float *qbar, const float *kbar, int BH, int nQ, int nKV, int D,
                          float c, float *scores, hipStream_t s);
-hipError_t launch_select(const float *scores, int R, int nKV, int m_k, float p, int p_all,
+// Also overwrites each row's slots of scores with its kept blocks in visit order (int32).
+hipError_t launch_select(float *scores, int R, int nKV, int ragged_last, int m_k, float p, int p_all,
                          uint32_t *bitmap, int nwords, int32_t *counts, hipStream_t s);
 hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, hipStream_t s);
 hipError_t launch_fill(const uint32_t *bitmap, int nwords, const int32_t *row_ptr, int R,
@@ -35,6 +36,7 @@ struct FwdArgs {
   void *o;
   float *lse;
   const int32_t *row_ptr, *col_idx, *row_order;
+  const int32_t *visit;    // NULL, or row r's kept blocks in visit order at visit[r * n_kvblk]
   const int32_t *q_order;  // NULL, or per head: query position -> storage row of q, o, lse
   const int32_t *kv_order; // NULL, or per head: key position -> storage row of k, v
   int B, H, N, D, block_q, block_kv, n_qblk, n_kvblk;
@@ -107,6 +109,7 @@ struct Fp8FwdArgs {
   uint16_t *o;              // [B, H, N, D] bf16
   float *lse;               // [B, H, N] or null
   const int32_t *row_ptr, *col_idx, *row_order;
+  const int32_t *visit;     // NULL, or row r's kept blocks in visit order at visit[r * n_kvblk]
   int B, H, N, D, block_q, n_qblk, n_kvblk;
   float scale_log2;         // log2(e) / sqrt(D)
 };

@@ -22,9 +22,10 @@
 // one pad granule per row, double-buffered: the next tile's loads are in flight while the
 // current tile is computed, with one barrier per tile. The V^T operand is read with the
 // transposing LDS read ds_read_b64_tr_b16, so V needs no transposition on the way in. The
-// ragged last KV block (if kept) is always the last tile of a row, because kept lists
-// are ascending; its rows past N reload the last valid row, and only that tile carries
-// the key mask.
+// tiles of a row come in the plan's visit order (pooled score descending, so the running
+// max settles early) or, without one, in ascending block order. Either way the ragged last
+// KV block (if kept) is the last tile of a row; its rows past N reload the last valid
+// row, and only that tile carries the key mask.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -168,7 +169,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     vgoff[m] = (r * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
   }
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
-  const int32_t *__restrict__ cols = a.col_idx + beg;
+  const int32_t *__restrict__ cols = a.visit ? a.visit + (size_t)row * a.n_kvblk : a.col_idx + beg;
 
   // Key positions through the plan's table (GATHER): key position p of this head is
   // storage row kvo[p]. The tile's 64 rows come one per lane (tabv, lane r = row r); a

@@ -81,6 +81,13 @@ typedef struct sa_plan {
   const int32_t *kv_order;   /* device [H*N] or NULL (caller-owned): key position j of head
                               * h is raster token kv_order[h*N + j]; NULL: k and v are
                               * already in key-position order */
+  int32_t *visit;            /* device, capacity R * n_kvblk, or NULL: row r's kept blocks
+                              * (the same set as its col_idx range) at visit[r * n_kvblk],
+                              * in the order the forward kernels visit them: pooled score
+                              * descending, ties to the lower block index, a kept ragged
+                              * last block moved to the end. It changes no result beyond
+                              * rounding order. NULL (plans from a caller's CSR and the
+                              * dense plan): the forward visits col_idx order. */
 } sa_plan;
 
 /* Accepted shapes: D in {64, 128}; block_q in {64, 128}; block_kv = 64; B*H <= 65535;

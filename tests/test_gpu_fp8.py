@@ -12,6 +12,9 @@ quantised for the forward pass), through the C ABI.
   the MFMA's accumulation and the bf16 store add far less. Bounds: rel-RMS 1e-2, max
   |dO| 3% of max |v|. lse: each rounded P lies within 2^-4 of P (relative) in the normal
   range, so the row sum, and lse, move by at most about 2^-4: bound 0.07.
+* Without the LSE output the kernel's running max is lazy (it trails the true max by up
+  to 2^4) and P is rounded as P * 2^4: the same relative rounding in the E4M3 normal
+  range, and the row sums still add the rounded values, so O is held to the same bars.
 * The distance to exact attention on the bf16 inputs is the format's own error (3
   mantissa bits on the logits) and is logged, not bounded tightly.
 """
@@ -118,11 +121,13 @@ def test_fwd_fp8_parity(case, qk):
     qd, kd, vd = _oracle_decoded(ent, w, qk)
     ref, ref_lse = sparse_attention(qd, kd, vd, rp, ci, w.block_q, 64, with_lse=True)
     rr, mx = _check(to_f64(o), ref, float(np.abs(vd).max()), case[0])
+    rr2, mx2 = _check(to_f64(sa.fwd_fp8(pack, plan)), ref, float(np.abs(vd).max()), case[0] + " no lse")
     dl = np.abs(lse.cpu().numpy() - ref_lse)
     assert float(dl.max()) <= TOL_LSE, f"lse: max {dl.max():.3e}"
     exact = sparse_attention(ent["q32"], ent["k32"], v32, rp, ci, w.block_q, 64)
     e = to_f64(o) - exact
-    log(f"{case[0]} {qk}: nnz {rp[-1]}; vs the low-bit oracle rel-RMS {rr:.2e}, max {mx:.2e}, lse max {dl.max():.2e}; "
+    log(f"{case[0]} {qk}: nnz {rp[-1]}; vs the low-bit oracle rel-RMS {rr:.2e}, max {mx:.2e} "
+        f"(without lse {rr2:.2e}, {mx2:.2e}), lse max {dl.max():.2e}; "
         f"vs exact attention on the bf16 inputs rel-RMS {np.sqrt((e ** 2).sum() / (exact ** 2).sum()):.2e}")
 
 
@@ -142,6 +147,9 @@ def test_fwd_fp8_empty_rows_and_ragged_only_row():
     qd, kd, vd = dequantize(*quantize_qkv(ent["q32"], ent["k32"], W.to_f32(ent["v"]), 64, 64), 64, 64)
     ref = sparse_attention(qd, kd, vd, rp, ci, 64, 64)
     _check(got, ref, float(np.abs(vd).max()), "edges")
+    o2 = to_f64(sa.fwd_fp8(pack, plan))
+    assert not o2[0, 0, 64:128].any()
+    _check(o2, ref, float(np.abs(vd).max()), "edges, no lse")
 
 
 def test_fwd_fp8_deterministic():

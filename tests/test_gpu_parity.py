@@ -13,7 +13,7 @@ import torch
 import block_sparse_attention_05_amd as sa
 import workloads as W
 from oracle import (oracle_plan, sparse_attention, dense_attention, dense_plan, exp_sa,
-                    topk_count)
+                    topk_count, block_scores, pool_blocks, score_scale)
 from tests.gpu_common import drop, check_out, inputs, log, sample_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -95,6 +95,36 @@ def test_plan_bitexact_small(case):
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_plan_visit_order(case):
+    """The plan's visit lists (the order in which the forward takes a row's kept tiles):
+    each row's kept set in the router's score order (descending, ties to the lower block
+    index), with a kept ragged last block moved to the end; when every block is kept by
+    rule (top_p >= 1 or m_k = nKV) the order is ascending."""
+    w = small_workload(*case)
+    log(f"visit order {w.name}")
+    ent = inputs(w)
+    p, (rp, ci) = gpu_plan(w, ent)
+    vl = p.visit_lists()
+    assert vl is not None
+    nq, nkv = w.n_qblk, w.n_kvblk
+    every = w.top_p >= 1.0 or topk_count(w.topk, nkv) >= nkv
+    ragged = w.N % w.block_kv != 0
+    for b in range(w.B):
+        for h in range(w.H):
+            S = block_scores(pool_blocks(ent["q32"][b, h], w.block_q),
+                             pool_blocks(ent["k32"][b, h], w.block_kv), score_scale(w.D))
+            for I in range(nq):
+                r = (b * w.H + h) * nq + I
+                kept = set(ci[rp[r]:rp[r + 1]].tolist())
+                order = range(nkv) if every else np.argsort(-S[I], kind="stable")
+                exp = [int(J) for J in order if int(J) in kept]
+                if ragged and nkv - 1 in kept:
+                    exp.remove(nkv - 1)
+                    exp.append(nkv - 1)
+                assert vl[r].tolist() == exp, (w.name, r)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_fwd_small(case):
     w = small_workload(*case)
     log(f"fwd {w.name}")
@@ -134,6 +164,17 @@ def test_plan_flat_and_near_flat_rows(scale):
     assert_same_csr(p.csr(), (rp, ci), f"flat {scale}")
     if scale == 0.0:
         assert np.all(np.diff(rp) == np.diff(rp)[0])
+    # visit lists from the full-sort path: the kept set in score order, ties ascending
+    vl = p.visit_lists()
+    q32, k32 = W.to_f32(q), W.to_f32(kb)
+    for h in range(w.H):
+        S = block_scores(pool_blocks(q32[0, h], w.block_q), pool_blocks(k32[0, h], w.block_kv),
+                         score_scale(w.D))
+        for I in (0, 7, w.n_qblk - 1):
+            r = h * w.n_qblk + I
+            kept = set(ci[rp[r]:rp[r + 1]].tolist())
+            exp = [int(J) for J in np.argsort(-S[I], kind="stable") if int(J) in kept]
+            assert vl[r].tolist() == exp, (scale, r)
 
 
 def test_dense_plan_matches_dense_oracle():
