@@ -159,7 +159,11 @@ size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_line
  * keeps every KV block), and o = alpha*Os + (1-alpha)*Ol (SLA2 page, item 2).
  * o: device [B, H, N, D] in dtype. lse: device float [B, H, N] or NULL; receives the
  * natural-log sum of exp(logits) over kept tokens (-inf for an empty row).
- * workspace: sparse_attn_fwd_workspace_bytes bytes (may be NULL when that is 0). */
+ * workspace: sparse_attn_fwd_workspace_bytes bytes (may be NULL when that is 0).
+ * Rounding: a row's tiles are taken in the plan's visit order (when it has one); for
+ * bf16 without lse the running max is lazy (it may trail the true max by up to 2^8 in
+ * the log2 domain), with lse it is exact. Both meet the same error bounds, but o may
+ * differ in its last bits between a call with lse and one without. */
 sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype dtype,
                           int B, int H, int N, int D, const sa_plan *plan,
                           const float *alpha, void *o, float *lse,
@@ -249,12 +253,15 @@ sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, 
 
 /* Block-sparse attention over the plan's kept tiles computed from an FP8 pack: the
  * products q k^T and P v run on fp8 MFMA with fp32 accumulation, the softmax in fp32,
- * and P (the probabilities scaled by 2^8 against the running maximum) is rounded to
- * E4M3 before it multiplies v; the row sums add the same rounded values.
+ * and P (the probabilities scaled by 2^8 against the running maximum, by 2^4 when the
+ * maximum is lazy) is rounded to E4M3 before it multiplies v; the row sums add the same
+ * rounded values.
  * pack: as sparse_attn_quantize_fp8 wrote it, with the plan's block_q and the same
  * qk_format (SA_QK_INT8: q k^T on int8 MFMA with exact int32 sums, scaled in fp32).
  * plan: a bf16 plan for [B, H, N, D] without a query order (else SA_ERR_UNSUPPORTED).
- * o: device [B, H, N, D] bf16. lse: device float [B, H, N] or NULL, as sparse_attn_fwd. */
+ * o: device [B, H, N, D] bf16. lse: device float [B, H, N] or NULL, as sparse_attn_fwd;
+ * without lse the running max is lazy (trailing by up to 2^4 in the log2 domain), so o
+ * may differ in its last bits from a call with lse. */
 sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format, int B, int H,
                               int N, int D, const sa_plan *plan, void *o, float *lse,
                               hipStream_t stream);
