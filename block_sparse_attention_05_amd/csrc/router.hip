@@ -282,12 +282,18 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
                                                      uint32_t *__restrict__ bitmap,
                                                      int nwords, int32_t *__restrict__ counts) {
   constexpr int P = 256 * ITEMS;
-  __shared__ uint64_t keys[P];
+  // the full sort's keys and the candidate path's buffers are never live together (the
+  // sort starts after the candidate path's last barrier), so they share one LDS region;
+  // with that, six rows fit on a CU at ITEMS = 8
+  constexpr int kCandBytes = kCandCap * (8 + 8 + 4);
+  constexpr int kPool = P * 8 > kCandBytes ? P * 8 : kCandBytes;
+  __shared__ __align__(16) char pool[kPool];
+  uint64_t *keys = reinterpret_cast<uint64_t *>(pool);
+  uint64_t *cand = reinterpret_cast<uint64_t *>(pool);
+  uint64_t *csort = cand + kCandCap;
+  float *cev = reinterpret_cast<float *>(csort + kCandCap);
   __shared__ float ev[P];
-  __shared__ uint32_t bits[kMaxKvBlocks / 32];
-  __shared__ uint64_t cand[kCandCap];
-  __shared__ uint64_t csort[kCandCap];
-  __shared__ float cev[kCandCap];
+  __shared__ uint32_t bits[P / 32];   // nwords <= P / 32
   __shared__ int hist[128];
   __shared__ unsigned long long hmass[128];   // per-bin sum of e in 2^-40 fixed point
   __shared__ float red[4];
