@@ -76,7 +76,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // four floats -> four E4M3 codes in one dword (byte u = value u)
 __device__ __forceinline__ uint32_t to_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion fills the low half-word and keeps the high one of its `old`
+  // operand, which the second then overwrites: any value will do there, and a's own bits
+  // (dead after this use) let the result take a's register with no zeroing move
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
