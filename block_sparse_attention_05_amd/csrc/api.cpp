@@ -382,7 +382,7 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
   // Only the first plan is exposed; the others run under the forwards before them.
   std::vector<hipEvent_t> ev;
   auto release = [&]() {
-    for (hipEvent_t e : ev) hipEventDestroy(e);   // released once the device is done with them
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);   // released once the device is done with them
   };
   if (two) {
     ev.resize(L.C + 1, nullptr);

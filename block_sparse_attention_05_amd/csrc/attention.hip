@@ -14,8 +14,8 @@
 // K tiles are staged row-major in LDS; V tiles are transposed on the way into LDS so the
 // V^T operand is a pair of 8-byte reads. The next tile's global loads are issued before
 // the current tile's math.
-// This file instantiates the kernel for fp32 inputs (fp64 scores, fp32 MFMA for P V);
-// bf16 inputs use the tuned kernel in sparse_fwd_bf16.hip.
+// This kernel serves fp32 inputs (fp64 scores and running max on the VALU, fp32 MFMA
+// for P V); bf16 inputs use the tuned kernel in sparse_fwd_bf16.hip.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,56 +27,14 @@
 namespace sa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBk = 64;  // keys per KV tile
+constexpr int kBk = 64;    // keys per KV tile
+constexpr int kVec = 4;    // fp32 elements per 16-byte load
+constexpr int kKPad = 4;   // LDS row padding of the K tile (elements)
+constexpr int kVPad = 4;   // LDS row padding of the V^T tile (elements)
 
-template <typename T>
-struct Elem;
-template <>
-struct Elem<uint16_t> {  // bf16 bit patterns
-  static constexpr int kVec = 8;      // elements per 16-byte load
-  static constexpr int kMfmaK = 16;   // reduction depth of one MFMA
-  static constexpr int kKPad = 8;     // LDS row padding of the K tile (elements)
-  static constexpr int kVPad = 4;     // LDS row padding of the V^T tile (elements)
-};
-template <>
-struct Elem<float> {
-  static constexpr int kVec = 4;
-  static constexpr int kMfmaK = 2;
-  static constexpr int kKPad = 4;
-  static constexpr int kVPad = 4;
-};
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  // round to nearest even; a and b are finite probabilities in [0, 1]
-  uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-  ua += 0x7fffu + ((ua >> 16) & 1u);
-  ub += 0x7fffu + ((ub >> 16) & 1u);
-  return (ua >> 16) | (ub & 0xffff0000u);
-}
-
-__device__ __forceinline__ float elem_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-__device__ __forceinline__ float elem_to_f32(float f) { return f; }
-
-template <typename T>
-__device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t *dst, float a, float b, float c, float d) {
-  uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b), uc = __float_as_uint(c),
-           ud = __float_as_uint(d);
-  ua += 0x7fffu + ((ua >> 16) & 1u);
-  ub += 0x7fffu + ((ub >> 16) & 1u);
-  uc += 0x7fffu + ((uc >> 16) & 1u);
-  ud += 0x7fffu + ((ud >> 16) & 1u);
-  uint2 w;
-  w.x = (ua >> 16) | (ub & 0xffff0000u);
-  w.y = (uc >> 16) | (ud & 0xffff0000u);
-  *reinterpret_cast<uint2 *>(dst) = w;
-}
-template <>
-__device__ __forceinline__ void store4<float>(float *dst, float a, float b, float c, float d) {
+__device__ __forceinline__ void store4(float *dst, float a, float b, float c, float d) {
   *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
 }
 
@@ -89,19 +47,18 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return (b % 8) * q + b / 8;
 }
 
-template <typename T, int D, int NW, bool LIN>
+template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
-  using E = Elem<T>;
+  using T = float;
   constexpr int NT = 64 * NW;             // threads
   constexpr int BQ = 32 * NW;             // queries per workgroup
-  constexpr int VEC = E::kVec;
-  constexpr int KROW = D + E::kKPad;      // K tile row stride (elements)
-  constexpr int VROW = kBk + E::kVPad;    // V^T tile row stride (elements)
+  constexpr int VEC = kVec;
+  constexpr int KROW = D + kKPad;         // K tile row stride (elements)
+  constexpr int VROW = kBk + kVPad;       // V^T tile row stride (elements)
   constexpr int KCH = kBk * D / VEC;      // 16-byte chunks per K tile
   constexpr int KPT = (KCH + NT - 1) / NT;
   constexpr int VCH = (kBk / 4) * (D / VEC);  // 4-row chunks per V tile
   constexpr int VPT = (VCH + NT - 1) / NT;
-  constexpr int KSTEPS = D / E::kMfmaK;   // MFMAs per 32x32 S^T block
   constexpr int DT = D / 32;              // 32-channel groups of O^T
 
   __shared__ __align__(16) T ks[kBk * KROW];
@@ -133,39 +90,19 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
   const int end = a.row_ptr[row + 1];
 
   if (beg == end) {
-    // no kept tile: Os = 0 (so O = (1 - alpha) * Ol with the linear branch), -inf LSE
+    // no kept tile: O = 0, LSE = -inf
     if (q_ok) {
-      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4) {
-        if constexpr (LIN) {
-          const int h = bh % a.H;
-          const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)h * D + d);
-          const float4 lv = *reinterpret_cast<const float4 *>(a.ol + head + (size_t)qi * D + d);
-          store4<T>(og + (size_t)qi * D + d, (1.f - al.x) * lv.x, (1.f - al.y) * lv.y,
-                    (1.f - al.z) * lv.z, (1.f - al.w) * lv.w);
-        } else {
-          store4<T>(og + (size_t)qi * D + d, 0.f, 0.f, 0.f, 0.f);
-        }
-      }
+      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4)
+        store4(og + (size_t)qi * D + d, 0.f, 0.f, 0.f, 0.f);
       if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = -INFINITY;
     }
     return;
   }
 
-  // Q operand. bf16: the B operand of S^T = K Q^T, 8 channels of this lane's query per
-  // MFMA step. fp32: the lane's whole query row (scores are formed on the VALU in fp64).
-  typedef typename std::conditional<sizeof(T) == 2, bf16x8_t, float>::type Frag;
-  constexpr int QREGS = sizeof(T) == 2 ? KSTEPS : D;
-  Frag qf[QREGS];
+  // the lane's whole query row (scores are formed on the VALU in fp64)
+  float qf[D];
 #pragma unroll
-  for (int s = 0; s < QREGS; ++s) {
-    if constexpr (sizeof(T) == 2) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (q_ok) w = *reinterpret_cast<const uint4 *>(qg + (size_t)qi * D + s * 16 + hf * 8);
-      qf[s] = __builtin_bit_cast(bf16x8_t, w);
-    } else {
-      qf[s] = q_ok ? qg[(size_t)qi * D + s] : 0.0f;
-    }
-  }
+  for (int s = 0; s < D; ++s) qf[s] = q_ok ? qg[(size_t)qi * D + s] : 0.0f;
 
   // staging registers for one K/V tile
   uint4 kr[KPT];
@@ -216,24 +153,10 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
         const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vr[u][1]);
         const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vr[u][2]);
         const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&vr[u][3]);
-        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            // columns 2m and 2m+1 of the four rows, as two rows of V^T
-            uint2 lo, hi;
-            lo.x = (w0[m] & 0xffffu) | (w1[m] << 16);
-            lo.y = (w2[m] & 0xffffu) | (w3[m] << 16);
-            hi.x = (w0[m] >> 16) | (w1[m] & 0xffff0000u);
-            hi.y = (w2[m] >> 16) | (w3[m] & 0xffff0000u);
-            *reinterpret_cast<uint2 *>(&vt[(col + 2 * m) * VROW + kgp * 4]) = lo;
-            *reinterpret_cast<uint2 *>(&vt[(col + 2 * m + 1) * VROW + kgp * 4]) = hi;
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            uint4 t4 = make_uint4(w0[m], w1[m], w2[m], w3[m]);
-            *reinterpret_cast<uint4 *>(&vt[(col + m) * VROW + kgp * 4]) = t4;
-          }
+        for (int m = 0; m < 4; ++m) {
+          uint4 t4 = make_uint4(w0[m], w1[m], w2[m], w3[m]);
+          *reinterpret_cast<uint4 *>(&vt[(col + m) * VROW + kgp * 4]) = t4;
         }
       }
     }
@@ -244,13 +167,10 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[t][i] = 0.0f;
-  // running max: scaled logits in the log2 domain (bf16), raw fp64 scores (fp32)
-  typedef typename std::conditional<sizeof(T) == 2, float, double>::type MaxT;
-  MaxT m_run = -INFINITY;
+  double m_run = -INFINITY;  // running max of the raw fp64 scores
   float l_run = 0.0f;       // this lane's part of the running sum
   const double sl2d = (double)a.scale_log2_f64;
 
-  const float sl2 = a.scale_log2;
   load_tile(a.col_idx[beg]);
 
   for (int it = beg; it < end; ++it) {
@@ -263,135 +183,63 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
     // ---- S^T = K Q^T for 64 keys x 32 queries (two 32-key blocks)
     floatx16 sacc[2];
     const int j0 = J * kBk;
-    if constexpr (sizeof(T) == 2) {
+    // fp32 inputs: scores in fp64 (exact products, fp64 sums), so large logits keep
+    // their small differences; the same (key, query) layout as the MFMA output.
+    double sd[2][16];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
+        const float *krow = reinterpret_cast<const float *>(&ks[key * KROW]);
+        double acc = 0.0;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const uint4 w = *reinterpret_cast<const uint4 *>(&ks[(kt * 32 + l32) * KROW + s * 16 + hf * 8]);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[s],
-                                                             sacc[kt], 0, 0, 0);
+        for (int d = 0; d < D; d += 4) {
+          const float4 kv = *reinterpret_cast<const float4 *>(krow + d);
+          acc = fma((double)qf[d], (double)kv.x, acc);
+          acc = fma((double)qf[d + 1], (double)kv.y, acc);
+          acc = fma((double)qf[d + 2], (double)kv.z, acc);
+          acc = fma((double)qf[d + 3], (double)kv.w, acc);
         }
+        sd[kt][i] = (j0 + key < N) ? acc : -INFINITY;
       }
-      // keys past the end of the sequence (ragged last tile)
-      if (j0 + kBk > N) {
+    double mx = sd[0][0];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
-            if (j0 + key >= N) sacc[kt][i] = -INFINITY;
-          }
+      for (int i = 0; i < 16; ++i) mx = fmax(mx, sd[kt][i]);
+    mx = fmax(mx, __shfl_xor(mx, 32));
+    const double m_new = fmax(m_run, mx);
+    const float corr = exp2f((float)((m_run - m_new) * sl2d));
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = exp2f((float)((sd[kt][i] - m_new) * sl2d));
+        sacc[kt][i] = pv;
+        psum += pv;
       }
-      // ---- online softmax (log2 domain)
-      float mx = sacc[0][0];
+    l_run = l_run * corr + psum;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float corr = exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = exp2f(sacc[kt][i] * sl2 - m_new);
-          sacc[kt][i] = pv;
-          psum += pv;
-        }
-      l_run = l_run * corr + psum;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][i] *= corr;
-    } else {
-      // fp32 inputs: scores in fp64 (exact products, fp64 sums), so large logits keep
-      // their small differences; the same (key, query) layout as the MFMA output.
-      double sd[2][16];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
-          const float *krow = reinterpret_cast<const float *>(&ks[key * KROW]);
-          double acc = 0.0;
-#pragma unroll
-          for (int d = 0; d < D; d += 4) {
-            const float4 kv = *reinterpret_cast<const float4 *>(krow + d);
-            acc = fma((double)qf[d], (double)kv.x, acc);
-            acc = fma((double)qf[d + 1], (double)kv.y, acc);
-            acc = fma((double)qf[d + 2], (double)kv.z, acc);
-            acc = fma((double)qf[d + 3], (double)kv.w, acc);
-          }
-          sd[kt][i] = (j0 + key < N) ? acc : -INFINITY;
-        }
-      double mx = sd[0][0];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmax(mx, sd[kt][i]);
-      mx = fmax(mx, __shfl_xor(mx, 32));
-      const double m_new = fmax(m_run, mx);
-      const float corr = exp2f((float)((m_run - m_new) * sl2d));
-      m_run = m_new;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = exp2f((float)((sd[kt][i] - m_new) * sl2d));
-          sacc[kt][i] = pv;
-          psum += pv;
-        }
-      l_run = l_run * corr + psum;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][i] *= corr;
-    }
+      for (int i = 0; i < 16; ++i) oacc[t][i] *= corr;
 
     // ---- O^T += V^T P^T. MFMA reduction index kk = hf*8 + e (e < 8) stands for key
     // base + (e/4)*8 + hf*4 + e%4, which is where the S^T layout put this lane's values.
-    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kt = s / 2, i0 = (s % 2) * 8;
-        const int base = kt * 32 + (s % 2) * 16;
-        uint4 pw;
-        pw.x = pack_bf16x2(sacc[kt][i0 + 0], sacc[kt][i0 + 1]);
-        pw.y = pack_bf16x2(sacc[kt][i0 + 2], sacc[kt][i0 + 3]);
-        pw.z = pack_bf16x2(sacc[kt][i0 + 4], sacc[kt][i0 + 5]);
-        pw.w = pack_bf16x2(sacc[kt][i0 + 6], sacc[kt][i0 + 7]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const T *vrow = &vt[(t * 32 + l32) * VROW + base + hf * 4];
-          uint4 vw;
-          const uint2 v0 = *reinterpret_cast<const uint2 *>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 8);
-          vw.x = v0.x; vw.y = v0.y; vw.z = v1.x; vw.w = v1.y;
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pb,
-                                                            oacc[t], 0, 0, 0);
+          const float av = vt[(t * 32 + l32) * VROW + key];
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sacc[kt][i], oacc[t], 0, 0, 0);
         }
       }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const float av = vt[(t * 32 + l32) * VROW + key];
-            oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sacc[kt][i], oacc[t], 0, 0, 0);
-          }
-        }
-    }
   }
 
   // ---- epilogue: normalise and store
@@ -406,34 +254,20 @@ __global__ __launch_bounds__(64 * NW) void sparse_fwd_kernel(FwdArgs a) {
         const int d = t * 32 + g * 8 + hf * 4;
         float o0 = oacc[t][g * 4 + 0] * inv, o1 = oacc[t][g * 4 + 1] * inv;
         float o2 = oacc[t][g * 4 + 2] * inv, o3 = oacc[t][g * 4 + 3] * inv;
-        if constexpr (LIN) {
-          // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel)
-          const int h = bh % a.H;
-          const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)h * D + d);
-          const float4 lv = *reinterpret_cast<const float4 *>(a.ol + head + (size_t)qi * D + d);
-          o0 = al.x * o0 + (1.f - al.x) * lv.x;
-          o1 = al.y * o1 + (1.f - al.y) * lv.y;
-          o2 = al.z * o2 + (1.f - al.z) * lv.z;
-          o3 = al.w * o3 + (1.f - al.w) * lv.w;
-        }
-        store4<T>(orow + d, o0, o1, o2, o3);
+        store4(orow + d, o0, o1, o2, o3);
       }
-    if (a.lse && hf == 0) {
-      if constexpr (sizeof(T) == 2)
-        a.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
-      else
-        a.lse[(size_t)bh * N + qi] = (float)((m_run * sl2d + (double)log2f(l_tot)) * 0.6931471805599453);
-    }
+    if (a.lse && hf == 0)
+      a.lse[(size_t)bh * N + qi] = (float)((m_run * sl2d + (double)log2f(l_tot)) * 0.6931471805599453);
   }
 }
 
-template <typename T, int D, bool LIN>
+template <int D>
 hipError_t launch_t(const FwdArgs &a, hipStream_t s) {
   const int R = a.B * a.H * a.n_qblk;
   if (a.block_q == 128)
-    sparse_fwd_kernel<T, D, 4, LIN><<<R, 256, 0, s>>>(a);
+    sparse_fwd_kernel<D, 4><<<R, 256, 0, s>>>(a);
   else
-    sparse_fwd_kernel<T, D, 2, LIN><<<R, 128, 0, s>>>(a);
+    sparse_fwd_kernel<D, 2><<<R, 128, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -442,7 +276,7 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t s) {
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s) {
   if (dt == SA_BF16) return launch_fwd_bf16(a, s);
   if (a.alpha != nullptr) return hipErrorNotSupported;
-  return a.D == 128 ? launch_t<float, 128, false>(a, s) : launch_t<float, 64, false>(a, s);
+  return a.D == 128 ? launch_t<128>(a, s) : launch_t<64>(a, s);
 }
 
 }  // namespace sa

@@ -118,8 +118,10 @@ __global__ void csc_count_kernel(const uint32_t *__restrict__ tbits, long C, int
 }
 
 // ---------------------------------------------------------------- dQ (row-major)
+// occupancy as in the forward: two waves per SIMD at NW = 4; at NW = 2 LDS allows two
+// workgroups per CU, one wave per SIMD
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int BQ = 32 * NW;
   constexpr int GR = D / 8 + 1;             // padded rows: one extra 16-byte granule

@@ -42,7 +42,7 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void tile_stats_bf16_kernel(const uint16_t *__restrict__ q,
                                                                   const uint16_t *__restrict__ k,
-                                                                  const float *__restrict__ lse, int H, int N,
+                                                                  const float *__restrict__ lse, int N,
                                                                   int n_qblk, int n_kvblk, float sl2,
                                                                   float *__restrict__ tmax,
                                                                   float *__restrict__ tmass) {
@@ -198,14 +198,14 @@ __global__ __launch_bounds__(64 * NW) void tile_stats_bf16_kernel(const uint16_t
 }
 
 template <int D>
-hipError_t launch_d(const void *q, const void *k, const float *lse, int BH, int H, int N, int bq,
+hipError_t launch_d(const void *q, const void *k, const float *lse, int BH, int N, int bq,
                     int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s) {
   const int R = BH * nQ;
   if (bq == 128)
-    tile_stats_bf16_kernel<D, 4><<<R, 256, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, lse, H, N, nQ,
+    tile_stats_bf16_kernel<D, 4><<<R, 256, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, lse, N, nQ,
                                                    nKV, sl2, tmax, tmass);
   else
-    tile_stats_bf16_kernel<D, 2><<<R, 128, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, lse, H, N, nQ,
+    tile_stats_bf16_kernel<D, 2><<<R, 128, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, lse, N, nQ,
                                                    nKV, sl2, tmax, tmass);
   return hipGetLastError();
 }
@@ -214,8 +214,9 @@ hipError_t launch_d(const void *q, const void *k, const float *lse, int BH, int 
 
 hipError_t launch_tile_stats(const void *q, const void *k, const float *lse, int BH, int H, int N, int D,
                              int bq, int nQ, int nKV, float sl2, float *tmax, float *tmass, hipStream_t s) {
-  if (D == 128) return launch_d<128>(q, k, lse, BH, H, N, bq, nQ, nKV, sl2, tmax, tmass, s);
-  return launch_d<64>(q, k, lse, BH, H, N, bq, nQ, nKV, sl2, tmax, tmass, s);
+  (void)H;   // rows are (batch, head) major; the kernel needs no head count of its own
+  if (D == 128) return launch_d<128>(q, k, lse, BH, N, bq, nQ, nKV, sl2, tmax, tmass, s);
+  return launch_d<64>(q, k, lse, BH, N, bq, nQ, nKV, sl2, tmax, tmass, s);
 }
 
 }  // namespace sa

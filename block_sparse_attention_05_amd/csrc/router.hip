@@ -62,9 +62,6 @@ __device__ __forceinline__ float exp_sa(float x) {
   return __builtin_ldexpf(p, (int)n);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(((uint32_t)b) << 16);
-}
 
 // ---------------------------------------------------------------- pooling
 // One thread owns 8 channels of one block and walks its tokens in order; D/8 threads

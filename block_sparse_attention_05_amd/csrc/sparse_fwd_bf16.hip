@@ -59,8 +59,6 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x4_t v;
   v[0] = (__bf16)a;
   v[1] = (__bf16)b;
@@ -69,10 +67,12 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint2, v);
 }
 
+// Two waves per SIMD with four-wave workgroups (two workgroups per CU by LDS). With
+// 64-query workgroups (NW = 2) the double-buffered K/V tiles still take 67.6 KB, so LDS
+// allows two workgroups, one wave per SIMD, and the register budget is not the limit.
 template <int D, int NW, bool LIN, bool GATHER>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1)))
 void sparse_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
   constexpr int GR = D / 8 + 1;             // K: 16-byte granules per LDS row (one pad granule)
   constexpr int ROWB = GR * 16;             // K: bytes per LDS row
