@@ -84,6 +84,46 @@ def test_plan_validation(lib):
     assert plan_call(lib, ws=FAKE + 64) == E.SA_ERR_WORKSPACE
 
 
+def test_plan_dense_validation(lib):
+    E = B
+
+    def dense(dt=0, shape=(1, 2, 1024, 64, 64, 64), ws=FAKE, wsb=1 << 40, out=True):
+        st = B.SaPlan()
+        return lib.sparse_attn_plan_dense(dt, *shape, ws, wsb, ctypes.byref(st) if out else None, None)
+
+    assert dense(out=False) == E.SA_ERR_INVALID_ARG
+    assert dense(dt=7) == E.SA_ERR_INVALID_ARG
+    assert dense(shape=(1, 2, 0, 64, 64, 64)) == E.SA_ERR_INVALID_ARG
+    assert dense(shape=(1, 2, 1024, 80, 64, 64)) == E.SA_ERR_UNSUPPORTED
+    assert dense(shape=(1, 2, 1024, 64, 64, 32)) == E.SA_ERR_UNSUPPORTED
+    assert dense(ws=None) == E.SA_ERR_WORKSPACE
+    assert dense(wsb=1000) == E.SA_ERR_WORKSPACE
+    assert dense(ws=FAKE + 64) == E.SA_ERR_WORKSPACE
+
+
+def test_plan_struct_matches_header():
+    """The ctypes mirror of sa_plan lists the header's fields in the header's order, with
+    pointers as pointers and 32-bit integers as c_int32 (a drift here would shift every
+    later field)."""
+    text = open(os.path.join(ROOT, "include", "sparse_attn.h")).read()
+    body = re.search(r"typedef struct sa_plan \{(.*?)\} sa_plan;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        ptr = "*" in decl
+        for name in re.sub(r"^(const\s+)?\w+\s*\*?", "", decl).replace("*", "").split(","):
+            fields.append((name.strip(), ptr))
+    mirror = [(n, t) for n, t in B.SaPlan._fields_]
+    assert [n for n, _ in fields] == [n for n, _ in mirror]
+    for (n, ptr), (_, t) in zip(fields, mirror):
+        assert (t is ctypes.c_void_p) == ptr, n
+        if not ptr:
+            assert t is ctypes.c_int32, n
+
+
 def csr_call(lib, rp, ci, shape=(1, 1, 256, 64, 64, 64)):
     st = B.SaPlan()
     rp = np.ascontiguousarray(rp, np.int32)
