@@ -302,12 +302,6 @@ def main():
         q_table = sa.cube_order(w.H, w.grid, qc)
         kv_table = sa.cube_order(w.H, w.grid, kc)
 
-    def move_in():
-        pass
-
-    def move_out():
-        pass
-
     def make_plan():
         if q_table is not None:
             return sa.plan_ordered(dq, dk, q_table, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws,
@@ -318,14 +312,10 @@ def main():
     o = torch.empty_like(dq)
 
     def step():
-        move_in()
         p = make_plan()
-        ev_mid.record(stream)
         sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
-        move_out()
         return p
 
-    ev_mid = torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
         p = step()
     torch.cuda.synchronize()
@@ -336,24 +326,17 @@ def main():
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    moved = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    fwd_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
         starts[i].record(stream)
-        move_in()
-        moved[i].record(stream)
         p = make_plan()
         mids[i].record(stream)
         sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
-        fwd_end[i].record(stream)
-        move_out()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_plan = [s.elapsed_time(m) for s, m in zip(moved, mids)]
-    ms_fwd = [m.elapsed_time(e) for m, e in zip(mids, fwd_end)]
-    ms_move = [a.elapsed_time(b) + c.elapsed_time(d) for a, b, c, d in zip(starts, moved, fwd_end, ends)]
+    ms_plan = [s.elapsed_time(m) for s, m in zip(starts, mids)]
+    ms_fwd = [m.elapsed_time(e) for m, e in zip(mids, ends)]
     t_step = float(np.mean(ms_step))
     t_fwd = float(np.mean(ms_fwd))
     t_plan = float(np.mean(ms_plan))
