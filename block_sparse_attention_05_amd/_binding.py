@@ -197,14 +197,18 @@ class Plan:
         ci = self.col_idx(int(rp[-1])).cpu().numpy()
         return rp, ci
 
-    def visit_lists(self) -> Optional[List[np.ndarray]]:
+    def visit_lists(self, rows: Optional[List[int]] = None):
         """Each row's kept blocks in the forward's visit order (host arrays; synchronises),
-        or None when the plan has no visit lists."""
+        or None when the plan has no visit lists. With ``rows``, a dict of those rows only
+        (copies just their lists)."""
         if not self.st.visit:
             return None
         rp = self.row_ptr().cpu().numpy().astype(np.int64)
         nkv = self.st.n_kvblk
-        full = self._view(self.st.visit, self.rows * nkv).view(self.rows, nkv).cpu().numpy()
+        full = self._view(self.st.visit, self.rows * nkv).view(self.rows, nkv)
+        if rows is not None:
+            return {r: full[r, :rp[r + 1] - rp[r]].cpu().numpy() for r in rows}
+        full = full.cpu().numpy()
         return [full[r, :rp[r + 1] - rp[r]].copy() for r in range(self.rows)]
 
 

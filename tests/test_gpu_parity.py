@@ -94,6 +94,19 @@ def test_plan_bitexact_small(case):
     assert_same_csr(got, (rp, ci), w.name)
 
 
+def visit_reference(S_row, kept, nkv, ragged, every):
+    """Host restatement of a row's visit order: its kept blocks by score, descending, ties
+    to the lower index (ascending when every block is kept by rule), a kept ragged last
+    block moved to the end."""
+    kept_set = set(int(J) for J in kept)
+    order = range(nkv) if every else np.argsort(-S_row, kind="stable")
+    out = [int(J) for J in order if int(J) in kept_set]
+    if ragged and nkv - 1 in kept_set:
+        out.remove(nkv - 1)
+        out.append(nkv - 1)
+    return out
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_plan_visit_order(case):
     """The plan's visit lists (the order in which the forward takes a row's kept tiles):
@@ -115,13 +128,8 @@ def test_plan_visit_order(case):
                              pool_blocks(ent["k32"][b, h], w.block_kv), score_scale(w.D))
             for I in range(nq):
                 r = (b * w.H + h) * nq + I
-                kept = set(ci[rp[r]:rp[r + 1]].tolist())
-                order = range(nkv) if every else np.argsort(-S[I], kind="stable")
-                exp = [int(J) for J in order if int(J) in kept]
-                if ragged and nkv - 1 in kept:
-                    exp.remove(nkv - 1)
-                    exp.append(nkv - 1)
-                assert vl[r].tolist() == exp, (w.name, r)
+                kept = ci[rp[r]:rp[r + 1]]
+                assert vl[r].tolist() == visit_reference(S[I], kept, nkv, ragged, every), (w.name, r)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
@@ -165,16 +173,16 @@ def test_plan_flat_and_near_flat_rows(scale):
     if scale == 0.0:
         assert np.all(np.diff(rp) == np.diff(rp)[0])
     # visit lists from the full-sort path: the kept set in score order, ties ascending
-    vl = p.visit_lists()
+    rows = [h * w.n_qblk + I for h in range(w.H) for I in (0, 7, w.n_qblk - 1)]
+    vl = p.visit_lists(rows=rows)
     q32, k32 = W.to_f32(q), W.to_f32(kb)
     for h in range(w.H):
         S = block_scores(pool_blocks(q32[0, h], w.block_q), pool_blocks(k32[0, h], w.block_kv),
                          score_scale(w.D))
         for I in (0, 7, w.n_qblk - 1):
             r = h * w.n_qblk + I
-            kept = set(ci[rp[r]:rp[r + 1]].tolist())
-            exp = [int(J) for J in np.argsort(-S[I], kind="stable") if int(J) in kept]
-            assert vl[r].tolist() == exp, (scale, r)
+            kept = ci[rp[r]:rp[r + 1]]
+            assert vl[r].tolist() == visit_reference(S[I], kept, w.n_kvblk, False, False), (scale, r)
 
 
 def test_dense_plan_matches_dense_oracle():
@@ -315,6 +323,16 @@ def test_workload_output_sampled(name, per_head):
     for (b, h, I), kept in sub.items():
         r = (b * w.H + h) * nq + I
         assert ci[rp[r]:rp[r + 1]].tolist() == kept.tolist(), (b, h, I)
+    # the sampled rows' visit lists against the oracle's scores
+    vl = p.visit_lists(rows=[(b * w.H + h) * nq + I for (b, h, I) in sub])
+    kbars = {}
+    for (b, h, I), kept in sub.items():
+        if (b, h) not in kbars:
+            kbars[(b, h)] = pool_blocks(ent["k32"][b, h], w.block_kv)
+        qbar = pool_blocks(ent["q32"][b, h, I * w.block_q:min(w.N, (I + 1) * w.block_q)], w.block_q)
+        S_row = block_scores(qbar, kbars[(b, h)], score_scale(w.D))[0]
+        r = (b * w.H + h) * nq + I
+        assert vl[r].tolist() == visit_reference(S_row, kept, w.n_kvblk, w.N % w.block_kv != 0, False), (b, h, I)
     o = sa.fwd(ent["dq"], ent["dk"], ent["dv"], p)
     ref = sparse_attention(ent["q32"], ent["k32"], W.to_f32(ent["v"]), rp, ci, w.block_q,
                            w.block_kv, rows=rows)
