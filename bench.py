@@ -272,7 +272,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path shards over heads with no exchange between GPUs, so N GPUs each run "
+              "this step on their share of the heads)", file=sys.stderr)
         sys.exit(2)
 
     import torch
