@@ -232,6 +232,13 @@ __device__ __forceinline__ uint32_t desc_order_bits(float f) {
   return ~asc;  // ascending in this value = descending in f
 }
 
+// the score a desc_order_bits key was made from (-0 comes back as +0, which exp_sa and
+// every comparison here treat alike)
+__device__ __forceinline__ float desc_order_value(uint32_t b) {
+  const uint32_t asc = ~b;
+  return __uint_as_float((asc & 0x80000000u) ? (asc & 0x7fffffffu) : ~asc);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -289,7 +296,11 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
   uint64_t *cand = reinterpret_cast<uint64_t *>(pool);
   uint64_t *csort = cand + kCandCap;
   float *cev = reinterpret_cast<float *>(csort + kCandCap);
-  __shared__ float ev[P];
+  // e_J by block index in LDS up to 8 items per thread; beyond that (more than 2,048
+  // blocks) e is recomputed from the sort keys instead, which saves 16 KB and lets four
+  // rows share a CU instead of three
+  constexpr bool kEvLds = ITEMS <= 8;
+  __shared__ float ev[kEvLds ? P : 1];
   __shared__ uint32_t bits[P / 32];   // nwords <= P / 32
   __shared__ int hist[128];
   __shared__ unsigned long long hmass[128];   // per-bin sum of e in 2^-40 fixed point
@@ -341,6 +352,7 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
 
   // e_J, the keys, and the in-thread part of the tree
   float tr[ITEMS];
+  float ee[ITEMS];   // this thread's e values when they are not kept in LDS
   uint64_t kv[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
@@ -348,7 +360,8 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
     const bool ok = J < nKV;
     const float e = ok ? exp_sa(sv[i] - m) : 0.0f;
     tr[i] = e;
-    ev[tid * ITEMS + i] = e;
+    if constexpr (kEvLds) ev[tid * ITEMS + i] = e;
+    else ee[i] = e;
     kv[i] = ok ? (((uint64_t)desc_order_bits(sv[i]) << 32) | (uint32_t)J) : ~0ull;
     if (ok) {
       const int b = __float_as_uint(e) >> 23;
@@ -435,7 +448,8 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int J = tid * ITEMS + i;
-      if (J < nKV && (int)(__float_as_uint(ev[J]) >> 23) >= bstar) {
+      const float eJ = kEvLds ? ev[kEvLds ? J : 0] : ee[i];
+      if (J < nKV && (int)(__float_as_uint(eJ) >> 23) >= bstar) {
         const int pos = atomicAdd(&sh_pos, 1);
         cand[pos] = kv[i];
       }
@@ -447,7 +461,7 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
       int rank = 0;
       for (int c2 = 0; c2 < ncand; ++c2) rank += cand[c2] < k ? 1 : 0;
       csort[rank] = k;
-      cev[rank] = ev[(uint32_t)k];
+      cev[rank] = kEvLds ? ev[kEvLds ? (uint32_t)k : 0] : exp_sa(desc_order_value((uint32_t)(k >> 32)) - m);
     }
     __syncthreads();
     if (wid == 0) {
@@ -507,18 +521,20 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
     }
   }
 
-  // e in score order
-  float es[ITEMS];
+  // e in score order (in LDS, or recomputed from the sorted keys by the scan below)
+  if constexpr (kEvLds) {
+    float es[ITEMS];
 #pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    const int r = tid + q * 256;
-    es[q] = 0.0f;
-    if (r < nKV) es[q] = ev[(uint32_t)keys[r]];
+    for (int q = 0; q < ITEMS; ++q) {
+      const int r = tid + q * 256;
+      es[q] = 0.0f;
+      if (r < nKV) es[q] = ev[(uint32_t)keys[r]];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) ev[tid + q * 256] = es[q];
+    __syncthreads();
   }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) ev[tid + q * 256] = es[q];
-  __syncthreads();
 
   // sequential top-p scan, one add at a time in score order. Wave 0 walks the sorted
   // values 64 at a time: each value is broadcast from its lane and added to a running
@@ -530,7 +546,11 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
     float acc = 0.0f;
     for (int c0 = 0; c0 < nKV; c0 += 64) {
       const bool in = c0 + lane < nKV;
-      const float val = in ? ev[c0 + lane] : 0.0f;
+      float val = 0.0f;
+      if (in) {
+        if constexpr (kEvLds) val = ev[c0 + lane];
+        else val = exp_sa(desc_order_value((uint32_t)(keys[c0 + lane] >> 32)) - m);
+      }
       const int vbits = __float_as_int(val);
       float pre = 0.0f;
 #pragma unroll

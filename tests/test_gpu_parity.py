@@ -158,12 +158,14 @@ def test_tie_breaks_to_lower_block():
     assert 11 not in set(ci.tolist()) or 5 in set(ci.tolist())
 
 
-@pytest.mark.parametrize("scale", [0.0, 1e-3, 0.3])
-def test_plan_flat_and_near_flat_rows(scale):
+@pytest.mark.parametrize("scale,nkv,H", [(0.0, 1100, 2), (1e-3, 1100, 2), (0.3, 1100, 2),
+                                         (0.0, 2500, 1), (1e-3, 2500, 1)])
+def test_plan_flat_and_near_flat_rows(scale, nkv, H):
     """Near-uniform pooled scores over 1,100 KV blocks put more than 512 blocks into the
     top exponent bin, so the router takes its full-sort path; a scale of 0 gives exact
-    ties everywhere (lowest block index first)."""
-    w = small_workload(f"flat{scale}", 1, 2, 64 * 1100, 64, "bf16", 128, 0.02, 0.9)
+    ties everywhere (lowest block index first). 2,500 blocks take the path with 16 items
+    per thread, where e is recomputed from the sort keys."""
+    w = small_workload(f"flat{scale}_{nkv}", 1, H, 64 * nkv, 64, "bf16", 128, 0.02, 0.9)
     q, k, v, _ = W.make_inputs(w)
     k32 = W.to_f32(k) * scale
     kb = W.f64_to_bf16_bits(k32.astype(np.float64))
