@@ -521,7 +521,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format
 
 namespace {
 struct BwdLayout {
-  size_t dvec, lse2, tbits, ccount, col_ptr, row_idx, total;
+  size_t dvec, lse2, tbits, ccount, col_ptr, row_idx, col_order, total;
   int nwq;
 };
 BwdLayout bwd_layout(const Shape &s) {
@@ -541,6 +541,7 @@ BwdLayout bwd_layout(const Shape &s) {
   L.ccount = take(C * 4);
   L.col_ptr = take((C + 1) * 4);
   L.row_idx = take((size_t)s.R * s.nKV * 4);
+  L.col_order = take(C * 4);
   L.total = off;
   return L;
 }
@@ -587,6 +588,7 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
   a.row_order = plan->row_order;
   a.col_ptr = reinterpret_cast<int32_t *>(ws + L.col_ptr);
   a.row_idx = reinterpret_cast<int32_t *>(ws + L.row_idx);
+  a.col_order = reinterpret_cast<int32_t *>(ws + L.col_order);
   a.B = B;
   a.H = H;
   a.N = N;

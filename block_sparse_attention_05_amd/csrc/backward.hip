@@ -9,7 +9,9 @@
 // Both gradient kernels recompute S and P; neither uses atomics, so every gradient is
 // summed in one fixed order and the results are deterministic. The CSC copy of the mask
 // (query blocks per KV block, ascending) is built from a column-major bitmap, whose
-// bits are set in any order, with the plan's row fill kernel.
+// bits are set in any order, with the plan's row fill kernel. The dK/dV workgroups take
+// their columns in the plan's balanced work order, built from the CSC counts: a head's
+// columns stay together on one XCD, and the XCDs get near-equal shares of kept tiles.
 //
 // MFMA layouts follow the forward kernel: 32x32x16 bf16 blocks, one wave per 32 rows of
 // the output it owns; a lane holds the 32 scores of one query (dQ kernel) or one key
@@ -353,7 +355,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int col = xcd_remap(blockIdx.x, gridDim.x);
+  const int col = a.col_order[xcd_remap(blockIdx.x, gridDim.x)];
   const int nKV = a.n_kvblk;
   const int bh = col / nKV;
   const int J = col - bh * nKV;
@@ -563,6 +565,9 @@ hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_scan(w.ccount, (int)C, a.col_ptr, s)) != hipSuccess) return e;
   if ((e = launch_fill(w.tbits, w.nwq, a.col_ptr, (int)C, a.row_idx, s)) != hipSuccess) return e;
+  // dkdv's work order: the plan's balance over the XCDs, applied to the columns (heads'
+  // column runs dealt heaviest first to the least-loaded XCD, ascending within a run)
+  if ((e = launch_row_order(a.col_ptr, (int)C, a.n_kvblk, a.col_order, s)) != hipSuccess) return e;
   // gradients
   if (a.D == 128) {
     if (a.block_q == 128) {

@@ -84,6 +84,7 @@ struct BwdArgs {
   uint16_t *dq, *dk, *dv;                  // [B, H, N, D] bf16
   const int32_t *row_ptr, *col_idx, *row_order;
   int32_t *col_ptr, *row_idx;              // CSC of the mask (workspace)
+  int32_t *col_order;                      // dkdv slot -> KV block column, balanced over XCDs (workspace)
   int B, H, N, D, block_q, n_qblk, n_kvblk;
   float scale;                             // 1/sqrt(D)
   float scale_log2;                        // log2(e)/sqrt(D)
