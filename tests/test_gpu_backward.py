@@ -117,10 +117,12 @@ def test_bwd_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-def test_bwd_480p_sampled():
-    """The 480p workload: dq on sampled query blocks, dk and dv on sampled KV blocks, each
-    against the oracle run on every query block those samples depend on."""
-    w = W.CONFIGS["wan13b_480p"]
+@pytest.mark.parametrize("workload", ["wan13b_480p", "wan14b_720p"])
+def test_bwd_workload_sampled(workload):
+    """Full-size workloads: dq on sampled query blocks, dk and dv on sampled KV blocks, each
+    against the oracle run on every query block those samples depend on. With 12 heads the
+    dK/dV work order splits heads into several runs per XCD; with 40 it deals whole heads."""
+    w = W.CONFIGS[workload]
     ent = inputs(w)
     do = _dout(w)
     plan = sa.plan(ent["dq"], ent["dk"], w.block_q, w.block_kv, w.topk, w.top_p)
@@ -147,5 +149,5 @@ def test_bwd_480p_sampled():
     for h, J in kcols:
         km[0, h, J * 64:min(w.N, (J + 1) * 64)] = True
     e = [_check(gq, rq, "dq", qm), _check(gk, rk, "dk", km), _check(gv, rv, "dv", km)]
-    log(f"480p sampled ({len(need)} query blocks in the oracle): " +
+    log(f"{workload} sampled ({len(need)} query blocks in the oracle): " +
         ", ".join(f"{a:.1e}/{b:.1e}" for a, b in e))
