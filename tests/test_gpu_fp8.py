@@ -165,11 +165,12 @@ def test_fwd_fp8_deterministic():
 
 
 @pytest.mark.parametrize("qk", QK)
-def test_fp8_480p_sampled(qk):
-    """The 480p workload: codes of sampled heads bit-exact, outputs of sampled query
-    blocks against the oracle."""
+@pytest.mark.parametrize("workload", ["wan13b_480p", "wan14b_720p"])
+def test_fp8_workload_sampled(workload, qk):
+    """Full-size workloads (720p is the shape the benchmark times): codes of sampled heads
+    bit-exact, outputs of sampled query blocks against the oracle."""
     from tests.gpu_common import sample_rows
-    w = W.CONFIGS["wan13b_480p"]
+    w = W.CONFIGS[workload]
     ent = inputs(w)
     plan = sa.plan(ent["dq"], ent["dk"], w.block_q, w.block_kv, w.topk, w.top_p)
     pack = sa.quantize_fp8(ent["dq"], ent["dk"], ent["dv"], w.block_q, qk=qk)
@@ -203,5 +204,5 @@ def test_fp8_480p_sampled(qk):
     for (b, hi, I), (ob, _) in ref.items():
         g.append(got[b, hi, I * w.block_q:min(w.N, (I + 1) * w.block_q)])
         r.append(ob)
-    rr, mx = _check(np.concatenate(g), np.concatenate(r), float(np.abs(vd).max()), "480p")
-    log(f"480p {qk} sampled ({len(rows)} query blocks): rel-RMS {rr:.2e}, max {mx:.2e}")
+    rr, mx = _check(np.concatenate(g), np.concatenate(r), float(np.abs(vd).max()), workload)
+    log(f"{workload} {qk} sampled ({len(rows)} query blocks): rel-RMS {rr:.2e}, max {mx:.2e}")
