@@ -180,3 +180,39 @@ def test_ordered_keys_through_table_equal_moved_keys(case):
         with pytest.raises(sa.SparseAttnError):
             sa.fwd(ent["dq"], ent["dk"], ent["dv"], p_tab, alpha=ent["dalpha"])
     log(f"{name}: keys through the table bitwise equal to moved keys (nnz {rp1[-1]})")
+
+
+def test_720p_tables_under_cube_tiling():
+    """The 720p shape as the benchmark runs it with cube tiling: queries and keys through
+    the plan's tables, nothing moved. On sampled heads the mask is bit-exact against the
+    oracle on host-permuted tensors, and sampled query blocks of o (taken to cube order)
+    are within the bf16 tolerance."""
+    from tests.gpu_common import sample_rows
+    w = W.CONFIGS["wan14b_720p"]
+    ent = inputs(w)
+    qc, kc = cubes_for(w.H, Q_CUBES), cubes_for(w.H, KV_CUBES)
+    qt = sa.cube_order(w.H, w.grid, qc)
+    kt = sa.cube_order(w.H, w.grid, kc)
+    p = sa.plan_ordered(ent["dq"], ent["dk"], qt, w.block_q, w.block_kv, w.topk, w.top_p, kv_order=kt)
+    rp, ci = p.csr()
+    o = sa.fwd(ent["dq"], ent["dk"], ent["dv"], p)
+    op = to_f64(sa.cube_permute(o, w.grid, qc))
+    hs = [0, 1, 2, w.H - 1]                       # every query and key cube shape, and the last head
+    q32p = permute_heads(ent["q32"][:, hs], w.grid, [qc[h] for h in hs])
+    k32p = permute_heads(ent["k32"][:, hs], w.grid, [kc[h] for h in hs])
+    v32p = permute_heads(W.to_f32(ent["v"][:, hs]), w.grid, [kc[h] for h in hs])
+    rrp, rci, _ = oracle_plan(q32p, k32p, w.block_q, w.block_kv, w.topk, w.top_p)
+    nq = w.n_qblk
+    for i, h in enumerate(hs):
+        for I in range(nq):
+            r, rr_ = h * nq + I, i * nq + I
+            assert np.array_equal(ci[rp[r]:rp[r + 1]], rci[rrp[rr_]:rrp[rr_ + 1]]), f"head {h} row {I}"
+    rows = sample_rows(w, 3, heads=[(0, i) for i in range(len(hs))])
+    ref = sparse_attention(q32p, k32p, v32p, rrp, rci, w.block_q, w.block_kv, rows=rows)
+    g, r = [], []
+    for (b, i, I), (ob, _) in ref.items():
+        g.append(op[b, hs[i], I * w.block_q:min(w.N, (I + 1) * w.block_q)])
+        r.append(ob)
+    mx, rr = check_out(np.concatenate(g), np.concatenate(r), "bf16", "720p cubes")
+    log(f"720p cube tiling through tables: masks of heads {hs} bit-exact (nnz {rp[-1]}), "
+        f"{len(rows)} sampled query blocks max |dO| {mx:.2e}, rel-RMS {rr:.2e}")
