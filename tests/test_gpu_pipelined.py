@@ -61,3 +61,24 @@ def test_pipelined_orders_with_caller_stream():
         snap = o.clone()                         # enqueued after the call
         torch.cuda.synchronize()
         assert torch.equal(snap.view(torch.int16), ref.view(torch.int16))
+
+
+def test_pipelined_720p_as_benchmarked():
+    """The 720p shape in the benchmark's launch configuration: 4 chunks on two streams, no
+    LSE output, one caller-owned output and workspace reused by back-to-back calls. Each
+    call is bitwise equal to the two-call path, whose output the parity tests check
+    against the oracle at this shape."""
+    w = W.CONFIGS["wan14b_720p"]
+    ent = inputs(w)
+    plan = sa.plan(ent["dq"], ent["dk"], w.block_q, w.block_kv, w.topk, w.top_p)
+    ref = sa.fwd(ent["dq"], ent["dk"], ent["dv"], plan)
+    ws = torch.empty(sa.pipelined_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv, 4),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(ref)
+    for call in range(2):
+        out.fill_(float("nan"))
+        sa.attention(ent["dq"], ent["dk"], ent["dv"], w.block_q, w.block_kv, w.topk, w.top_p, chunks=4,
+                     out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref)), f"call {call}"
+    log("720p: pipelined over 4 chunks, workspace reused, bitwise equal to the two-call path")
