@@ -1,7 +1,7 @@
 // Backward of block-sparse attention for gfx950 (the pages fine-tune through the sparse
 // kernel: SpargeAttention2 page, section 2; SLA2 page). For query block I with kept KV
 // tiles K_I, c = 1/sqrt(D), P = exp(c * Q K^T - lse) (the forward's log-sum-exp):
-//   Dv  = rowsum(dO * O)                       dvec_kernel
+//   Dv  = rowsum(dO * O)        formed by bwd_dq_kernel at row start
 //   dS  = P * (dO V^T - Dv)
 //   dQ  = c * dS K        over each row's kept tiles          bwd_dq_kernel (CSR)
 //   dK  = c * dS^T Q,  dV = P^T dO   over each KV block's query blocks
@@ -60,39 +60,6 @@ __device__ __forceinline__ float bf(uint32_t w, int hi) {
 }
 
 // ---------------------------------------------------------------- Dv = rowsum(dO * O)
-// Per head, rows 0 .. NP-1 of the padded arrays: Dv and lse*log2(e) for n < N, and 0 and
-// +inf past N, so that padded query rows get P = 0 and dS = 0 wherever they are read.
-template <int D>
-__global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *__restrict__ o,
-                                                   const uint16_t *__restrict__ dout,
-                                                   const float *__restrict__ lse, int N, int NP, long rows,
-                                                   float *__restrict__ dvec, float *__restrict__ lse2) {
-  constexpr int TPR = D / 8;   // lanes per query row
-  const long r = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // padded row bh*NP + n
-  const int l = threadIdx.x % TPR;
-  const long bh = r / NP;
-  const int n = (int)(r - bh * NP);
-  const bool ok = r < rows && n < N;
-  float acc = 0.0f;
-  if (ok) {
-    const long src = bh * N + n;
-    const uint4 a = *reinterpret_cast<const uint4 *>(o + src * D + l * 8);
-    const uint4 b = *reinterpret_cast<const uint4 *>(dout + src * D + l * 8);
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      acc = acc + bf(aw[c], 0) * bf(bw[c], 0);
-      acc = acc + bf(aw[c], 1) * bf(bw[c], 1);
-    }
-  }
-#pragma unroll
-  for (int m = TPR / 2; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m);
-  if (r < rows && l == 0) {
-    dvec[r] = acc;
-    lse2[r] = ok ? lse[bh * N + n] * kLog2e : INFINITY;
-  }
-}
-
 // ---------------------------------------------------------------- CSC of the mask
 __global__ void zero_words_kernel(uint32_t *__restrict__ p, long n) {
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = 0u;
@@ -161,10 +128,19 @@ void bwd_dq_kernel(BwdArgs a) {
   const bool q_ok = qi < N;
   const int beg = a.row_ptr[row];
   const int end = a.row_ptr[row + 1];
+  // The row's entries of the per-head padded arrays that the dK/dV kernel reads: Dv and
+  // lse*log2(e) for n < N, 0 and +inf past N (padded query rows then get P = 0 and dS = 0),
+  // and the same for a row with no kept tile, whose queries no KV block visits.
+  float *dv_out = a.dvec + (size_t)bh * a.NP + qi;
+  float *lse2_out = a.lse2 + (size_t)bh * a.NP + qi;
   if (beg == end) {
     if (q_ok)
       for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4)
         *reinterpret_cast<uint2 *>(dqg + (size_t)qi * D + d) = make_uint2(0u, 0u);
+    if (hf == 0) {
+      *dv_out = 0.0f;
+      *lse2_out = INFINITY;
+    }
     return;
   }
 
@@ -179,9 +155,29 @@ void bwd_dq_kernel(BwdArgs a) {
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
     dof[s] = __builtin_bit_cast(bf16x8_t, x);
   }
-  // a query past N has lse2 = +inf in the padded array, so its P (and dS) is 0
-  const float lse2 = a.lse2[(size_t)bh * a.NP + qi];
-  const float dv = a.dvec[(size_t)bh * a.NP + qi];
+  // Dv = rowsum(dO * O): this lane's 64 channels (those of its dO fragments) in ascending
+  // order, then the other half's sum from the partner lane
+  float dpart = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    uint4 ow = make_uint4(0, 0, 0, 0);
+    if (q_ok) ow = *reinterpret_cast<const uint4 *>(a.o + head + (size_t)qi * D + s * 16 + hf * 8);
+    const uint4 dw = __builtin_bit_cast(uint4, dof[s]);
+    const uint32_t oa[4] = {ow.x, ow.y, ow.z, ow.w}, da[4] = {dw.x, dw.y, dw.z, dw.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      dpart = dpart + bf(oa[c], 0) * bf(da[c], 0);
+      dpart = dpart + bf(oa[c], 1) * bf(da[c], 1);
+    }
+  }
+  const float dpo = __shfl_xor(dpart, 32);
+  const float dv = dpart + dpo;   // the same in both lanes: the sum commutes
+  // a query past N gets lse2 = +inf, so its P (and dS) is 0
+  const float lse2 = q_ok ? a.lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
+  if (hf == 0) {
+    *dv_out = dv;
+    *lse2_out = lse2;
+  }
   const float sl2 = a.scale_log2;
 
   uint32_t goff[NIW];
@@ -544,16 +540,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s) {
   const int BH = a.B * a.H;
-  const long rows = (long)BH * a.NP;
   hipError_t e;
-  // Dv and lse * log2(e), padded per head to NP rows
-  if (a.D == 128)
-    dvec_kernel<128><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a.o, a.dout, a.lse, a.N, a.NP, rows, a.dvec,
-                                                                  a.lse2);
-  else
-    dvec_kernel<64><<<(unsigned)((rows + 31) / 32), 256, 0, s>>>(a.o, a.dout, a.lse, a.N, a.NP, rows, a.dvec,
-                                                                 a.lse2);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   // CSC of the mask
   const int R = BH * a.n_qblk;
   const long C = (long)BH * a.n_kvblk;
