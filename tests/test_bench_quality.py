@@ -43,3 +43,28 @@ def test_cpu_baseline_walks_heads_within_budget():
     assert f"heads 0..{w.H - 1}" in res["sample"]
     one = bench.cpu_baseline(w, q, k, v, rp, ci, budget_s=0.0)     # stops after the first head
     assert "heads 0..0" in one["sample"]
+
+
+def test_more_than_one_gpu_is_refused_before_any_work():
+    """--gpus above 1 exits with status 2 and a message, before torch or the library loads."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_traffic_needs_the_profiled_kernel_source(tmp_path, monkeypatch):
+    """The committed HBM bytes are reported only for the kernel source they were taken on."""
+    import json
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"w": {"kernel_source_sha256_16": bench.source_hash(),
+                                   "hbm_bytes_per_launch": 123}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.traffic_for("w", 1.0) == 123
+    assert bench.traffic_for("other", 1.0) is None
+    f.write_text(json.dumps({"w": {"kernel_source_sha256_16": "0" * 16, "hbm_bytes_per_launch": 123}}))
+    assert bench.traffic_for("w", 1.0) is None
