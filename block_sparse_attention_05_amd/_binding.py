@@ -41,6 +41,7 @@ class SaPlan(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("row_order", ctypes.c_void_p),
         ("q_order", ctypes.c_void_p), ("kv_order", ctypes.c_void_p), ("visit", ctypes.c_void_p),
+        ("nnz", ctypes.c_void_p),
     ]
 
 
@@ -74,7 +75,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_plan_dense.restype = i32
     lib.sparse_attn_plan_from_csr.argtypes = [i32] * 7 + [vp, vp, vp, sz, pplan, vp]
     lib.sparse_attn_plan_from_csr.restype = i32
-    lib.sparse_attn_fwd_workspace_bytes.argtypes = [i32] * 5
+    lib.sparse_attn_fwd_workspace_bytes.argtypes = [pplan, i32]
     lib.sparse_attn_fwd_workspace_bytes.restype = sz
     lib.sparse_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd.restype = i32
@@ -190,6 +191,12 @@ class Plan:
 
     def row_order(self):
         return self._view(self.st.row_order, self.rows)
+
+    def nnz(self):
+        """The plan's device scalar holding the number of kept blocks (int64, one element)."""
+        torch = _torch()
+        off = self.st.nnz - self.ws.data_ptr()
+        return self.ws[off:off + 8].view(torch.int64)
 
     def csr(self) -> Tuple[np.ndarray, np.ndarray]:
         """(row_ptr, col_idx) copied to host numpy arrays (synchronises)."""
@@ -337,7 +344,7 @@ def fwd(q, k, v, plan: Plan, alpha=None, return_lse: bool = False, out=None, lse
     o = out if out is not None else torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    need = lib.sparse_attn_fwd_workspace_bytes(B, H, N, D, 1 if alpha is not None else 0)
+    need = lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(plan.st), 1 if alpha is not None else 0)
     ws = workspace
     if need > 0 and ws is None:
         ws = _new_ws(need, q.device)
@@ -396,12 +403,15 @@ class Fp8Pack:
         B, H, N, D = self.shape
         BH = B * H
         nQ, nKV = -(-N // self.block_q), -(-N // 64)
-        sizes = [("q8", BH * N * D), ("k8", BH * N * D), ("vt8", BH * nKV * D * 64),
-                 ("qe", BH * nQ * 4), ("ke", BH * nKV * 4), ("ve", BH * D * 4), ("vamax", BH * D * 4)]
+        # (name, bytes used, bytes reserved): q's exponents are reserved for 64-query blocks
+        sizes = [("q8", BH * N * D, BH * N * D), ("k8", BH * N * D, BH * N * D),
+                 ("vt8", BH * nKV * D * 64, BH * nKV * D * 64), ("qe", BH * nQ * 4, BH * nKV * 4),
+                 ("ke", BH * nKV * 4, BH * nKV * 4), ("ve", BH * D * 4, BH * D * 4),
+                 ("vamax", BH * D * 4, BH * D * 4), ("tail", 0, 4 * self.block_q)]
         off, out = 0, {}
-        for name, n in sizes:
+        for name, n, cap in sizes:
             out[name] = (off, n)
-            off = (off + n + 255) & ~255
+            off = (off + cap + 255) & ~255
         return out
 
     def part(self, name: str):

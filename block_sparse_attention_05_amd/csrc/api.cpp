@@ -36,7 +36,7 @@ bool dtype_ok(int dt) { return dt == SA_BF16 || dt == SA_FP32; }
 
 // Plan workspace layout (each piece 256-byte aligned).
 struct PlanLayout {
-  size_t row_ptr, col_idx, row_order, counts, bitmap, qbar, kbar, scores, total;
+  size_t row_ptr, col_idx, row_order, counts, bitmap, qbar, kbar, scores, nnz, total;
 };
 
 PlanLayout plan_layout(const Shape &s) {
@@ -56,6 +56,7 @@ PlanLayout plan_layout(const Shape &s) {
   L.qbar = take((size_t)s.B * s.H * s.nQ * s.D * 4);
   L.kbar = take((size_t)s.B * s.H * s.nKV * s.D * 4);
   L.scores = take((size_t)s.B * s.H * s.nQ * s.nKV * 4);
+  L.nnz = take(8);
   L.total = off;
   return L;
 }
@@ -84,6 +85,7 @@ void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L
   p->q_order = nullptr;
   p->kv_order = nullptr;
   p->visit = nullptr;
+  p->nnz = reinterpret_cast<int64_t *>(ws + L.nnz);
 }
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
@@ -171,7 +173,7 @@ sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, 
   if (e == hipSuccess)
     e = launch_select(scores, (int)s.R, s.nKV, N % block_kv != 0, m_k, p32, p_all, bitmap, nwords, counts,
                       stream);
-  if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, stream);
+  if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, p.nnz, stream);
   if (e == hipSuccess) e = launch_fill(bitmap, nwords, p.row_ptr, (int)s.R, p.col_idx, stream);
   if (e == hipSuccess)
     e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
@@ -210,7 +212,7 @@ sa_status sparse_attn_plan_dense(sa_dtype dtype, int B, int H, int N, int D, int
   if (st != SA_OK) return st;
   sa_plan p;
   fill_plan(&p, s, dtype, static_cast<char *>(workspace), L);
-  hipError_t e = launch_dense_plan((int)s.R, s.nKV, p.row_ptr, p.col_idx, stream);
+  hipError_t e = launch_dense_plan((int)s.R, s.nKV, p.row_ptr, p.col_idx, p.nnz, stream);
   if (e == hipSuccess)
     e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
@@ -251,6 +253,8 @@ sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, 
                                 hipMemcpyHostToDevice, stream);
   if (e == hipSuccess && nnz > 0)
     e = hipMemcpyAsync(p.col_idx, host_col_idx, (size_t)nnz * 4, hipMemcpyHostToDevice, stream);
+  const int64_t nnz64 = nnz;   // read by the copy before the synchronisation below
+  if (e == hipSuccess) e = hipMemcpyAsync(p.nnz, &nnz64, 8, hipMemcpyHostToDevice, stream);
   // the host arrays may be pageable and reused as soon as this call returns
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e == hipSuccess)
@@ -260,9 +264,10 @@ sa_status sparse_attn_plan_from_csr(sa_dtype dtype, int B, int H, int N, int D, 
   return SA_OK;
 }
 
-size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_linear) {
+size_t sparse_attn_fwd_workspace_bytes(const sa_plan *plan, int with_linear) {
+  if (plan == nullptr) return 0;
   Shape s;
-  if (check_shape(B, H, N, D, 64, 64, &s) != SA_OK) return 0;
+  if (check_shape(plan->B, plan->H, plan->N, plan->D, plan->block_q, plan->block_kv, &s) != SA_OK) return 0;
   return fwd_layout(s, with_linear).total;
 }
 
@@ -426,8 +431,11 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
 }
 
 namespace {
+// The q exponent part is sized for 64-query blocks whatever block_q is, and the pack ends
+// in a tail of 4*block_q bytes, so packs for block_q 64 and 128 never have the same size;
+// both calls require the exact size, which rejects a pack made for another block_q.
 struct Fp8Layout {
-  size_t q8, k8, vt8, qe, ke, ve, vamax, total;
+  size_t q8, k8, vt8, qe, ke, ve, vamax, tail, total;
 };
 Fp8Layout fp8_layout(const Shape &s) {
   Fp8Layout L{};
@@ -441,10 +449,11 @@ Fp8Layout fp8_layout(const Shape &s) {
   L.q8 = take(BH * s.N * s.D);
   L.k8 = take(BH * s.N * s.D);
   L.vt8 = take(BH * s.nKV * s.D * 64);
-  L.qe = take(BH * s.nQ * 4);
+  L.qe = take(BH * ceil_div(s.N, 64) * 4);
   L.ke = take(BH * s.nKV * 4);
   L.ve = take(BH * s.D * 4);
   L.vamax = take(BH * s.D * 4);
+  L.tail = take((size_t)s.bq * 4);
   L.total = off;
   return L;
 }
@@ -469,6 +478,7 @@ sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, 
   const Fp8Layout L = fp8_layout(s);
   st = check_ws(pack, pack_bytes, L.total);
   if (st != SA_OK) return st;
+  if (pack_bytes != L.total) return SA_ERR_WORKSPACE;
   char *pk = static_cast<char *>(pack);
   Fp8Pack p{reinterpret_cast<uint8_t *>(pk + L.q8),   reinterpret_cast<uint8_t *>(pk + L.k8),
             reinterpret_cast<uint8_t *>(pk + L.vt8),  reinterpret_cast<int32_t *>(pk + L.qe),
@@ -494,6 +504,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format
   const Fp8Layout L = fp8_layout(s);
   st = check_ws(pack, pack_bytes, L.total);
   if (st != SA_OK) return st;
+  if (pack_bytes != L.total) return SA_ERR_PLAN_MISMATCH;   // a pack made for another block_q
   const char *pk = static_cast<const char *>(pack);
   Fp8FwdArgs a{};
   a.q8 = reinterpret_cast<const uint8_t *>(pk + L.q8);
@@ -521,7 +532,7 @@ sa_status sparse_attn_fwd_fp8(const void *pack, size_t pack_bytes, int qk_format
 
 namespace {
 struct BwdLayout {
-  size_t dvec, lse2, tbits, ccount, col_ptr, row_idx, col_order, total;
+  size_t dvec, lse2, tbits, ccount, col_ptr, row_idx, col_order, cnnz, total;
   int nwq;
 };
 BwdLayout bwd_layout(const Shape &s) {
@@ -542,6 +553,7 @@ BwdLayout bwd_layout(const Shape &s) {
   L.col_ptr = take((C + 1) * 4);
   L.row_idx = take((size_t)s.R * s.nKV * 4);
   L.col_order = take(C * 4);
+  L.cnnz = take(8);
   L.total = off;
   return L;
 }
@@ -602,6 +614,7 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
   w.tbits = reinterpret_cast<uint32_t *>(ws + L.tbits);
   w.nwq = L.nwq;
   w.ccount = reinterpret_cast<int32_t *>(ws + L.ccount);
+  w.cnnz = reinterpret_cast<int64_t *>(ws + L.cnnz);
   return hip_status(launch_bwd(a, w, stream));
 }
 

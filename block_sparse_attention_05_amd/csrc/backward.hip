@@ -550,7 +550,7 @@ hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s) {
                                                               w.nwq, w.tbits);
   csc_count_kernel<<<(unsigned)((C + 255) / 256), 256, 0, s>>>(w.tbits, C, w.nwq, w.ccount);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_scan(w.ccount, (int)C, a.col_ptr, s)) != hipSuccess) return e;
+  if ((e = launch_scan(w.ccount, (int)C, a.col_ptr, w.cnnz, s)) != hipSuccess) return e;
   if ((e = launch_fill(w.tbits, w.nwq, a.col_ptr, (int)C, a.row_idx, s)) != hipSuccess) return e;
   // dkdv's work order: the plan's balance over the XCDs, applied to the columns (heads'
   // column runs dealt heaviest first to the least-loaded XCD, ascending within a run)

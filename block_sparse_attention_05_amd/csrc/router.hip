@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
 
 // ---------------------------------------------------------------- CSR
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ counts, int R,
-                                                    int32_t *__restrict__ row_ptr) {
+                                                    int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz) {
   __shared__ int wsum[16];
   __shared__ int carry;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -620,6 +620,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ 
     if (tid == 1023) carry = incl;
     __syncthreads();
   }
+  if (tid == 0) *nnz = carry;
 }
 
 // One wave per row: popcounts, a lane prefix sum, then each lane writes its words' set
@@ -652,14 +653,17 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint32_t *__restrict__ 
 }
 
 __global__ void dense_plan_kernel(int R, int nKV, int32_t *__restrict__ row_ptr,
-                                  int32_t *__restrict__ col_idx) {
+                                  int32_t *__restrict__ col_idx, int64_t *__restrict__ nnz) {
   const long total = (long)R * nKV;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (long)gridDim.x * blockDim.x) {
     col_idx[i] = (int32_t)(i % nKV);
     if (i % nKV == 0) row_ptr[i / nKV] = (int32_t)i;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[R] = (int32_t)total;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    row_ptr[R] = (int32_t)total;
+    *nnz = total;
+  }
 }
 
 // Work order for the forward kernels. A forward launch of R workgroups runs workgroup b
@@ -826,8 +830,8 @@ hipError_t launch_select(float *scores, int R, int nKV, int ragged_last, int m_k
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, hipStream_t s) {
-  scan_kernel<<<1, 1024, 0, s>>>(counts, R, row_ptr);
+hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, int64_t *nnz, hipStream_t s) {
+  scan_kernel<<<1, 1024, 0, s>>>(counts, R, row_ptr, nnz);
   return hipGetLastError();
 }
 
@@ -837,12 +841,12 @@ hipError_t launch_fill(const uint32_t *bitmap, int nwords, const int32_t *row_pt
   return hipGetLastError();
 }
 
-hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, int64_t *nnz, hipStream_t s) {
   const long total = (long)R * nKV;
   long blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  dense_plan_kernel<<<(unsigned)blocks, 256, 0, s>>>(R, nKV, row_ptr, col_idx);
+  dense_plan_kernel<<<(unsigned)blocks, 256, 0, s>>>(R, nKV, row_ptr, col_idx, nnz);
   return hipGetLastError();
 }
 

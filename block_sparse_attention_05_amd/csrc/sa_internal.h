@@ -23,10 +23,11 @@ hipError_t launch_scores(const float *qbar, const float *kbar, int BH, int nQ, i
 // Also overwrites each row's slots of scores with its kept blocks in visit order (int32).
 hipError_t launch_select(float *scores, int R, int nKV, int ragged_last, int m_k, float p, int p_all,
                          uint32_t *bitmap, int nwords, int32_t *counts, hipStream_t s);
-hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, hipStream_t s);
+// also writes the total (row_ptr[R]) to *nnz as int64
+hipError_t launch_scan(const int32_t *counts, int R, int32_t *row_ptr, int64_t *nnz, hipStream_t s);
 hipError_t launch_fill(const uint32_t *bitmap, int nwords, const int32_t *row_ptr, int R,
                        int32_t *col_idx, hipStream_t s);
-hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+hipError_t launch_dense_plan(int R, int nKV, int32_t *row_ptr, int32_t *col_idx, int64_t *nnz, hipStream_t s);
 hipError_t launch_row_order(const int32_t *row_ptr, int R, int nQ, int32_t *row_order, hipStream_t s);
 hipError_t launch_router_exp(const float *x, float *y, int64_t n, hipStream_t s);
 
@@ -93,6 +94,7 @@ struct BwdBufs {
   uint32_t *tbits;   // [B*H*n_kvblk, nwq] column-major bitmap of the mask
   int nwq;           // ceil(n_qblk / 32)
   int32_t *ccount;   // [B*H*n_kvblk]
+  int64_t *cnnz;     // the CSC's total (written by the scan, not read)
 };
 hipError_t launch_bwd(const BwdArgs &a, const BwdBufs &w, hipStream_t s);
 // Low-bit forward (fp8.hip): OCP FP8 E4M3 codes with power-of-two group exponents.

@@ -88,6 +88,11 @@ typedef struct sa_plan {
                               * last block moved to the end. It changes no result beyond
                               * rounding order. NULL (plans from a caller's CSR and the
                               * dense plan): the forward visits col_idx order. */
+  int64_t *nnz;              /* device scalar in the workspace: the number of kept blocks,
+                              * equal to row_ptr[R]; written by the plan calls on their
+                              * stream, so it may be read once that stream has reached the
+                              * end of the call (a device-side consumer needs no host
+                              * round trip to size its work) */
 } sa_plan;
 
 /* Accepted shapes: D in {64, 128}; block_q in {64, 128}; block_kv = 64; B*H <= 65535;
@@ -148,8 +153,9 @@ sa_status sparse_attn_plan_ordered(const void *q, const void *k, sa_dtype dtype,
                                    const int32_t *kv_order, void *workspace, size_t ws_bytes,
                                    sa_plan *out, hipStream_t stream);
 
-/* Workspace bytes sparse_attn_fwd needs: 0 without the linear branch. */
-size_t sparse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int with_linear);
+/* Workspace bytes sparse_attn_fwd needs with this plan: 0 without the linear branch
+ * (with_linear = 0); 0 as well when plan is NULL or describes an unsupported shape. */
+size_t sparse_attn_fwd_workspace_bytes(const sa_plan *plan, int with_linear);
 
 /* Block-sparse attention over the plan's kept tiles (SpargeAttention2 page, section 2(3)).
  * q, k, v: device [B, H, N, D] in dtype; the shapes and dtype must equal the plan's.
@@ -235,17 +241,23 @@ sa_status sparse_attn_bwd(const void *q, const void *k, const void *v, const voi
  *                                   block; keys past N hold 0;
  *   qe     int32 [B, H, nQ]         exponents of the q groups (nQ = ceil(N/block_q));
  *                                   with SA_QK_INT8 the fp32 scales s, as bit patterns;
+ *                                   the part is sized for B*H*ceil(N/64) entries, of
+ *                                   which the first B*H*nQ are used;
  *   ke     int32 [B, H, nKV]        exponents of the k groups (nKV = ceil(N/64)); likewise;
  *   ve     int32 [B, H, D]          exponents of the v groups;
- *   vamax  uint32 [B, H, D]         the quantiser's scratch (per-channel max |v|). */
+ *   vamax  uint32 [B, H, D]         the quantiser's scratch (per-channel max |v|);
+ *   tail   4*block_q bytes          unused; it makes the pack's size depend on block_q.
+ * Both calls below require pack_bytes to equal sparse_attn_fp8_pack_bytes for their
+ * shape and block sizes, and packs for block_q 64 and 128 always differ in size, so a
+ * pack quantised for another block_q than the plan's is rejected. */
 size_t sparse_attn_fp8_pack_bytes(int B, int H, int N, int D, int block_q, int block_kv);
 
 typedef enum { SA_QK_E4M3 = 0, SA_QK_INT8 = 1 } sa_qk_format;
 
 /* Quantises q, k, v (device [B, H, N, D] bf16, finite) into pack (device, 256-byte
- * aligned, pack_bytes >= sparse_attn_fp8_pack_bytes). block_q must be the block_q of the
- * plans the pack will be used with; block_kv must be 64. fp32 inputs: SA_ERR_UNSUPPORTED.
- * Deterministic. */
+ * aligned, pack_bytes == sparse_attn_fp8_pack_bytes, else SA_ERR_WORKSPACE). block_q
+ * must be the block_q of the plans the pack will be used with; block_kv must be 64.
+ * fp32 inputs: SA_ERR_UNSUPPORTED. Deterministic. */
 sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, sa_dtype dtype,
                                    int B, int H, int N, int D, int block_q, int block_kv,
                                    int qk_format, void *pack, size_t pack_bytes,
@@ -257,7 +269,10 @@ sa_status sparse_attn_quantize_fp8(const void *q, const void *k, const void *v, 
  * maximum is lazy) is rounded to E4M3 before it multiplies v; the row sums add the same
  * rounded values.
  * pack: as sparse_attn_quantize_fp8 wrote it, with the plan's block_q and the same
- * qk_format (SA_QK_INT8: q k^T on int8 MFMA with exact int32 sums, scaled in fp32).
+ * qk_format (SA_QK_INT8: q k^T on int8 MFMA with exact int32 sums, scaled in fp32);
+ * pack_bytes must equal sparse_attn_fp8_pack_bytes for the plan's shape and block_q
+ * (SA_ERR_PLAN_MISMATCH otherwise, SA_ERR_WORKSPACE when it is smaller). The format is
+ * not recorded in the pack: a pack read with the other qk_format gives meaningless o.
  * plan: a bf16 plan for [B, H, N, D] without a query order (else SA_ERR_UNSUPPORTED).
  * o: device [B, H, N, D] bf16. lse: device float [B, H, N] or NULL, as sparse_attn_fwd;
  * without lse the running max is lazy (trailing by up to 2^4 in the log2 domain), so o

@@ -55,7 +55,15 @@ def test_workspace_sizes(lib):
     # the workspace holds at least the CSR at full capacity
     R, nkv = 40 * 591, 1182
     assert f(1, 40, 75600, 128, 128, 64) >= 4 * (R + 1 + R * nkv)
-    assert lib.sparse_attn_fwd_workspace_bytes(1, 12, 32760, 128, 0) == 0
+    st = B.SaPlan()
+    st.B, st.H, st.N, st.D, st.block_q, st.block_kv = 1, 12, 32760, 128, 128, 64
+    assert lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 0) == 0
+    lin = lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 1)
+    # at least H and z per head, and Ol in fp32
+    assert lin >= 12 * (128 * 128 + 128) * 4 + 12 * 32760 * 128 * 4
+    assert lib.sparse_attn_fwd_workspace_bytes(None, 1) == 0
+    st.D = 96
+    assert lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 1) == 0
 
 
 def plan_call(lib, q=FAKE, k=FAKE, dt=0, shape=(1, 2, 1024, 64, 64, 64), topk=0.25, p=0.9,
@@ -163,7 +171,7 @@ def test_fwd_validation(lib):
     no_rows = (1, 2, 1024, 64, 64, 64, 16, 16, 0, 0, None, None, None)
     assert fwd_call(lib, no_rows) == B.SA_ERR_INVALID_ARG
     # the linear branch needs its workspace
-    need = lib.sparse_attn_fwd_workspace_bytes(1, 2, 1024, 64, 1)
+    need = lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(B.SaPlan(*good)), 1)
     if need > 0:
         assert fwd_call(lib, good, alpha=FAKE) == B.SA_ERR_WORKSPACE
         assert fwd_call(lib, good, alpha=FAKE, ws=FAKE, wsb=need - 1) == B.SA_ERR_WORKSPACE
@@ -288,7 +296,9 @@ def _fp8_layout_bytes(B_, H, N, D, bq):
     """The pack size from the layout the header documents, summed independently."""
     BH, nQ, nKV = B_ * H, -(-N // bq), -(-N // 64)
     off = 0
-    for n in (BH * N * D, BH * N * D, BH * nKV * D * 64, 4 * BH * nQ, 4 * BH * nKV, 4 * BH * D, 4 * BH * D):
+    # q's exponents are reserved for 64-query blocks; a tail of 4 * block_q bytes ends the pack
+    for n in (BH * N * D, BH * N * D, BH * nKV * D * 64, 4 * BH * nKV, 4 * BH * nKV, 4 * BH * D, 4 * BH * D,
+              4 * bq):
         off = (off + n + 255) // 256 * 256
     return off
 
@@ -302,6 +312,16 @@ def test_fp8_pack_bytes(lib):
         assert offs["vamax"][0] + offs["vamax"][1] <= f(*shape, 64)
     assert f(1, 1, 1024, 96, 64, 64) == 0
     assert f(1, 1, 1024, 64, 64, 128) == 0
+
+
+def test_fp8_pack_sizes_differ_by_block_q(lib):
+    """The two block_q values never give packs of one size, so the exact-size check in
+    both calls tells a pack quantised for 64-query blocks from one for 128."""
+    f = lib.sparse_attn_fp8_pack_bytes
+    for BH in (1, 2, 3, 5, 8, 12, 40):
+        for N in list(range(1, 3000, 37)) + [8192, 32760, 65536, 75600, 245760]:
+            a, b = f(1, BH, N, 64, 64, 64), f(1, BH, N, 64, 128, 64)
+            assert a > 0 and b > 0 and a != b, (BH, N)
 
 
 def test_fp8_quantize_and_fwd_validation(lib):
@@ -342,6 +362,11 @@ def test_fp8_quantize_and_fwd_validation(lib):
     assert fwd(o=None) == B.SA_ERR_INVALID_ARG
     assert fwd(pb=need - 1) == B.SA_ERR_WORKSPACE
     assert fwd(shape=(1, 2, 2048, 64)) == B.SA_ERR_PLAN_MISMATCH
+    # a pack sized for another block_q (larger here) is rejected, not read at wrong offsets
+    need128 = lib.sparse_attn_fp8_pack_bytes(1, 2, 1024, 64, 128, 64)
+    assert need128 > need
+    assert fwd(pb=need128) == B.SA_ERR_PLAN_MISMATCH
+    assert quant(pb=need128) == B.SA_ERR_WORKSPACE
     st.dtype = 1
     assert fwd() == B.SA_ERR_UNSUPPORTED                    # fp32 plans
     st.dtype = 0

@@ -147,6 +147,21 @@ def test_fwd_small(case):
     check_out(to_f64(sa.fwd(ent["dq"], ent["dk"], ent["dv"], p)), ref, w.dtype, w.name + " no lse")
 
 
+def test_plan_nnz_scalar():
+    """The plan's device nnz scalar equals row_ptr[R] for the router's plan, the dense
+    plan and a caller's CSR."""
+    w = small_workload("nnz", 2, 3, 3000, 128, "bf16", 128, 0.05, 0.9)
+    ent = inputs(w)
+    p, (rp, ci) = gpu_plan(w, ent)
+    assert int(p.nnz().item()) == int(rp[-1]) == ci.size
+    pd = sa.plan_dense(ent["dq"], 128, 64)
+    assert int(pd.nnz().item()) == w.rows * w.n_kvblk
+    rows = [np.arange(0, w.n_kvblk, 3)] * w.rows
+    crp = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    pc = sa.plan_from_csr(ent["dq"], crp, np.concatenate(rows).astype(np.int32), 128, 64)
+    assert int(pc.nnz().item()) == int(crp[-1])
+
+
 def test_tie_breaks_to_lower_block():
     w = small_workload("ties", 1, 2, 1024, 64, "bf16", 64, 1.0 / 16, 0.0)
     q, k, v, _ = W.make_inputs(w)
