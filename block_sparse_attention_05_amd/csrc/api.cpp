@@ -335,6 +335,34 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
 }
 
 namespace {
+// Events that order the pipelined call's two streams, made once per thread and device and
+// reused by every later call. Re-recording an event is safe while earlier waits on it are
+// still pending: a wait takes the record that precedes it. Never destroyed (they live as
+// long as the thread's HIP context); NULL when an event cannot be made.
+hipEvent_t *pipeline_events(int n) {
+  struct Pool {
+    int device = -1;
+    std::vector<hipEvent_t> ev;
+  };
+  thread_local std::vector<Pool> pools;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  Pool *p = nullptr;
+  for (auto &x : pools)
+    if (x.device == dev) p = &x;
+  if (p == nullptr) {
+    pools.push_back(Pool{});
+    p = &pools.back();
+    p->device = dev;
+  }
+  while ((int)p->ev.size() < n) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    p->ev.push_back(e);
+  }
+  return p->ev.data();
+}
+
 // The pipelined call splits the B*H heads into chunks of `per` heads, each planned in its
 // own plan workspace.
 struct PipeLayout {
@@ -385,26 +413,13 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
   const bool two = aux_stream != stream;
   // Plans go on aux_stream back to back; forwards on `stream`, each after its chunk's plan.
   // Only the first plan is exposed; the others run under the forwards before them.
-  std::vector<hipEvent_t> ev;
-  auto release = [&]() {
-    for (hipEvent_t e : ev) (void)hipEventDestroy(e);   // released once the device is done with them
-  };
+  hipEvent_t *ev = nullptr;
   if (two) {
-    ev.resize(L.C + 1, nullptr);
-    for (auto &e : ev)
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
-        e = nullptr;
-        st = SA_ERR_HIP;
-      }
+    ev = pipeline_events(L.C + 1);
+    if (ev == nullptr) return SA_ERR_HIP;
     // the plans start after the caller's earlier work on `stream` (inputs written there)
-    if (st == SA_OK && (hipEventRecord(ev[L.C], stream) != hipSuccess ||
-                        hipStreamWaitEvent(aux_stream, ev[L.C], 0) != hipSuccess))
-      st = SA_ERR_HIP;
-    if (st != SA_OK) {
-      ev.erase(std::remove(ev.begin(), ev.end(), nullptr), ev.end());
-      release();
-      return st;
-    }
+    if (hipEventRecord(ev[L.C], stream) != hipSuccess || hipStreamWaitEvent(aux_stream, ev[L.C], 0) != hipSuccess)
+      return SA_ERR_HIP;
   }
   std::vector<sa_plan> plans(L.C);
   for (int c = 0; c < L.C && st == SA_OK; ++c) {
@@ -426,7 +441,6 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
                          chunk(c, static_cast<const char *>(v)), dtype, 1, hc, N, D, &plans[c], nullptr,
                          const_cast<char *>(chunk(c, static_cast<const char *>(o))), lc, nullptr, 0, stream);
   }
-  release();
   return st;
 }
 

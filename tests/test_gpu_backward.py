@@ -1,18 +1,20 @@
 """GPU parity of the block-sparse attention backward (dq, dk, dv) against the float64
 oracle, through the C ABI.
 
-Two references. The first is the oracle with Dv = rowsum(dO * o) formed from the
-forward's output as stored (bf16), which is what the kernels do; against it the only
-differences are the kernels' own roundings: P and dS go to bf16 before their MFMA
-products (2^-9 relative each) and the gradients are stored in bf16 (2^-9). Each gradient
-sums many such terms with mixed signs, so the bound is rel-RMS 1e-2 and max |d| within
-3e-2 of the largest reference magnitude. The second is the exact gradient. There the
-rounding of o to bf16 also enters: it shifts Dv, and dQ = c * sum_j dS_ij k_j turns that
-shift into c * dDv_i * sum_j P_ij k_j, which the keys' shared components (positional
-term, sinks) do not cancel. Its size depends on the case (rel-RMS 1.1e-2 on the small
-ragged case, 3.4e-2 when 37 tokens share one block), and the oracle gives it exactly:
-by the triangle inequality the kernel is within that distance plus its own bounds
-(rel-RMS 1e-2, max 3%) of the exact gradient. Zero gradients (empty rows, KV blocks no row keeps) must be exactly zero.
+The reference is the oracle with Dv = rowsum(dO * o) formed from the forward's output
+as stored (bf16), which is what the kernels take, as any backward that reuses the
+forward's output does. Against it the only differences are the kernels' own roundings:
+P and dS go to bf16 before their MFMA products (2^-9 relative each) and the gradients
+are stored in bf16 (2^-9). Each gradient sums many such terms with mixed signs, so the
+bound is rel-RMS 1e-2 and max |d| within 3e-2 of the largest reference magnitude.
+
+The distance to the exact gradient (Dv from the exact o) is logged, not asserted: the
+rounding of o to bf16 shifts Dv, and dQ = c * sum_j dS_ij k_j turns that shift into
+c * dDv_i * sum_j P_ij k_j, which the keys' shared components (positional term, sinks)
+do not cancel. It is a property of the stored o, not of the kernels, and the oracle
+gives it exactly (rel-RMS of dQ about 1e-2 on the ragged cases, 3.4e-2 when 37 tokens
+share one block). Zero gradients (empty rows, KV blocks no row keeps) must be exactly
+zero.
 """
 import numpy as np
 import pytest
@@ -34,7 +36,7 @@ def _dout(w, seed=7):
     return W.f64_to_bf16_bits(rng.normal(size=(w.B, w.H, w.N, w.D)))
 
 
-def _check(got, ref, what, mask=None, rrms=TOL_RRMS, max_extra=0.0):
+def _check(got, ref, what, mask=None, rrms=TOL_RRMS):
     g = to_f64(got)
     if mask is not None:
         g, ref = g[mask], ref[mask]
@@ -44,7 +46,7 @@ def _check(got, ref, what, mask=None, rrms=TOL_RRMS, max_extra=0.0):
     mx = float(err.max())
     assert np.all(np.isfinite(g)), f"{what}: non-finite"
     assert rr <= rrms, f"{what}: rel-RMS {rr:.3e}"
-    assert mx <= TOL_MAX_REL * scale + max_extra, f"{what}: max |d| {mx:.3e} vs max |ref| {scale:.3e}"
+    assert mx <= TOL_MAX_REL * scale, f"{what}: max |d| {mx:.3e} vs max |ref| {scale:.3e}"
     return rr, mx / scale
 
 
@@ -78,14 +80,15 @@ def test_bwd_small(case):
     rq, rk, rv = sparse_attention_backward(*args, o=o)
     e = [_check(gq, rq, "dq"), _check(gk, rk, "dk"), _check(gv, rv, "dv")]
     exact = sparse_attention_backward(*args)
-    x = []
-    for g, st, ex, what in zip((gq, gk, gv), (rq, rk, rv), exact, ("dq", "dk", "dv")):
-        inherent = float(np.sqrt(((st - ex) ** 2).sum()) / np.sqrt((ex ** 2).sum()))   # bf16 o alone
-        x.append(_check(g, ex, what + " exact", rrms=inherent + TOL_RRMS,
-                        max_extra=float(np.abs(st - ex).max())))
+
+    def rrms(a, b):
+        return float(np.sqrt(((a - b) ** 2).sum()) / max(np.sqrt((b ** 2).sum()), 1e-300))
+
+    inherent = [rrms(st, ex) for st, ex in zip((rq, rk, rv), exact)]      # bf16 o alone
+    kernel = [rrms(to_f64(g), ex) for g, ex in zip((gq, gk, gv), exact)]
     log(f"{name}: nnz {rp[-1]}; rel-RMS / max rel vs the stored-o reference: " +
-        ", ".join(f"{a:.1e}/{b:.1e}" for a, b in e) + "; vs exact: " +
-        ", ".join(f"{a:.1e}/{b:.1e}" for a, b in x))
+        ", ".join(f"{a:.1e}/{b:.1e}" for a, b in e) + "; rel-RMS to the exact gradient, "
+        "stored-o reference / kernel: " + ", ".join(f"{a:.1e}/{b:.1e}" for a, b in zip(inherent, kernel)))
 
 
 def test_bwd_empty_rows_and_unkept_blocks_are_zero():
