@@ -29,7 +29,7 @@ EXPORTS = (
     "sparse_attn_plan_ordered", "sparse_attn_tile_stats", "sparse_attn_cube_permute",
     "sparse_attn_cube_order", "sparse_attn_fp8_pack_bytes", "sparse_attn_quantize_fp8",
     "sparse_attn_fwd_fp8", "sparse_attn_router_exp", "sparse_attn_status_string",
-    "sparse_attn_version",
+    "sparse_attn_version", "sparse_attn_pipelined_noalloc",
 )
 
 
@@ -94,6 +94,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_pipelined_workspace_bytes.restype = sz
     lib.sparse_attn_pipelined.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [dbl, dbl, i32, vp, vp, vp, sz, vp, vp]
     lib.sparse_attn_pipelined.restype = i32
+    lib.sparse_attn_pipelined_noalloc.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, vp, vp]
+    lib.sparse_attn_pipelined_noalloc.restype = i32
     lib.sparse_attn_fp8_pack_bytes.argtypes = [i32] * 6
     lib.sparse_attn_fp8_pack_bytes.restype = sz
     lib.sparse_attn_quantize_fp8.argtypes = [vp, vp, vp, i32] + [i32] * 7 + [vp, sz, vp]
@@ -520,6 +522,24 @@ def attention(q, k, v, block_q: int = 128, block_kv: int = 64, topk: float = 0.0
                                      lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(),
                                      s.cuda_stream, aux.cuda_stream), "sparse_attn_pipelined")
     return (o, lse) if return_lse else o
+
+
+def attention_noalloc(q, k, v, block_q: int = 128, block_kv: int = 64, topk: float = 0.05,
+                      top_p: float = 0.9, out=None, lse=None, stream=None):
+    """Plan and forward for all heads on one stream with the library's static scratch (see
+    sparse_attn_pipelined_noalloc): nothing is allocated when ``out`` (and ``lse``, if
+    wanted) are given. Returns o, or (o, lse) when lse is given."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    _check_qkv(q, o)
+    _check(lib.sparse_attn_pipelined_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, N,
+                                             D, block_q, block_kv, float(topk), float(top_p), o.data_ptr(),
+                                             lse.data_ptr() if lse is not None else None, _stream(stream)),
+           "sparse_attn_pipelined_noalloc")
+    return (o, lse) if lse is not None else o
 
 
 def tile_stats(q, k, lse, block_q: int = 128, block_kv: int = 64, stream=None):

@@ -5,11 +5,20 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "sa_internal.h"
 
 using namespace sa;
+
+// Scratch of sparse_attn_pipelined_noalloc: the plan workspace of one chunk of heads at a
+// time. Every device the library runs on holds its own copy for the life of the process.
+// Host code never passes this name to a kernel (on the host it only stands for the
+// symbol): it uses the device address that hipGetSymbolAddress returns for the current
+// device, kept per device below.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -440,6 +449,68 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
     st = sparse_attn_fwd(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)),
                          chunk(c, static_cast<const char *>(v)), dtype, 1, hc, N, D, &plans[c], nullptr,
                          const_cast<char *>(chunk(c, static_cast<const char *>(o))), lc, nullptr, 0, stream);
+  }
+  return st;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char *scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device.
+sa_status device_scratch(char **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SA_ERR_HIP;
+    scratch_ptr[dev] = static_cast<char *>(p);
+  }
+  *out = scratch_ptr[dev];
+  return SA_OK;
+}
+}  // namespace
+
+sa_status sparse_attn_pipelined_noalloc(const void *q, const void *k, const void *v, sa_dtype dtype, int B,
+                                        int H, int N, int D, int block_q, int block_kv, double topk_frac,
+                                        double top_p, void *o, float *lse, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return SA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
+  if (!(topk_frac >= 0.0 && topk_frac <= 1.0) || !(top_p >= 0.0 && top_p <= 1.0)) return SA_ERR_INVALID_ARG;
+  Shape s;
+  sa_status st = check_shape(B, H, N, D, block_q, block_kv, &s);
+  if (st != SA_OK) return st;
+  // the largest chunk of heads whose plan workspace fits, then chunks of equal size
+  const int BH = B * H;
+  auto plan_bytes = [&](int heads) {
+    Shape s1;
+    return check_shape(1, heads, N, D, block_q, block_kv, &s1) == SA_OK ? plan_layout(s1).total : (size_t)-1;
+  };
+  if (plan_bytes(1) > kScratchBytes) return SA_ERR_WORKSPACE;   // one head's plan does not fit
+  int per = 1;
+  while (per < BH && plan_bytes(per + 1) <= kScratchBytes) ++per;
+  const int C = ceil_div(BH, per);
+  per = ceil_div(BH, C);
+  char *ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != SA_OK) return st;
+  const size_t esz = dtype == SA_BF16 ? 2 : 4;
+  const size_t head_bytes = (size_t)N * D * esz;
+  // one stream: chunk c's plan follows chunk c-1's forward, so the chunks share the scratch
+  for (int c = 0; c < C && st == SA_OK; ++c) {
+    const int hc = BH - c * per < per ? BH - c * per : per;
+    const size_t off = (size_t)c * per * head_bytes;
+    sa_plan p;
+    st = plan_impl(static_cast<const char *>(q) + off, static_cast<const char *>(k) + off, dtype, 1, hc, N, D,
+                   block_q, block_kv, topk_frac, top_p, nullptr, nullptr, ws, kScratchBytes, &p, stream);
+    if (st != SA_OK) break;
+    st = sparse_attn_fwd(static_cast<const char *>(q) + off, static_cast<const char *>(k) + off,
+                         static_cast<const char *>(v) + off, dtype, 1, hc, N, D, &p, nullptr,
+                         static_cast<char *>(o) + off, lse ? lse + (size_t)c * per * N : nullptr, nullptr, 0,
+                         stream);
   }
   return st;
 }

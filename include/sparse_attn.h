@@ -202,6 +202,25 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
                                 float *lse, void *workspace, size_t ws_bytes,
                                 hipStream_t stream, hipStream_t aux_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sparse_attn_pipelined with one stream
+ * and no workspace argument. The plan workspaces live in a static device array of the
+ * library, 128 MiB per device (every device the library runs on holds it until the
+ * process ends). Heads are taken in chunks of equal size, as many heads per chunk as fit
+ * in that array; each chunk is planned and then attended on `stream` before the next
+ * chunk reuses the array. The call allocates nothing (no hipMalloc, hipFree or event);
+ * its first call on a device looks up the array's device address once.
+ * o and lse equal those of sparse_attn_plan + sparse_attn_fwd (and of
+ * sparse_attn_pipelined) bit for bit. Arguments as for sparse_attn_pipelined;
+ * SA_ERR_WORKSPACE when one head's plan workspace (sparse_attn_plan_workspace_bytes
+ * with B = H = 1) exceeds 128 MiB. Every call on a device shares the one array and
+ * leaves its last plan in it: calls on one stream are ordered, but calls on one device
+ * that are not ordered with each other (other streams, other threads) race. */
+sa_status sparse_attn_pipelined_noalloc(const void *q, const void *k, const void *v, sa_dtype dtype,
+                                        int B, int H, int N, int D, int block_q, int block_kv,
+                                        double topk_frac, double top_p, void *o, float *lse,
+                                        hipStream_t stream);
+
 /* Workspace bytes sparse_attn_bwd needs for this shape. */
 size_t sparse_attn_bwd_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv);
 

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert len(decl) == 20
+    assert len(decl) == 21
     assert sorted(B.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -375,6 +375,30 @@ def test_fp8_quantize_and_fwd_validation(lib):
     st.q_order = None
     st.row_ptr = None
     assert fwd() == B.SA_ERR_INVALID_ARG
+
+
+def test_pipelined_noalloc_validation(lib):
+    """Host checks of the allocation-free call, before it touches the device: null
+    pointers, k or p out of range, unsupported shapes, and a shape whose single-head plan
+    exceeds the 128 MiB static scratch."""
+    f = lib.sparse_attn_pipelined_noalloc
+
+    def call(q=FAKE, o=FAKE, dt=0, shape=(1, 2, 1024, 64, 64, 64), topk=0.1, p=0.9):
+        return f(q, FAKE, FAKE, dt, *shape, topk, p, o, None, None)
+
+    assert call(q=None) == B.SA_ERR_INVALID_ARG
+    assert call(o=None) == B.SA_ERR_INVALID_ARG
+    assert call(dt=5) == B.SA_ERR_INVALID_ARG
+    assert call(topk=1.5) == B.SA_ERR_INVALID_ARG
+    assert call(p=-0.1) == B.SA_ERR_INVALID_ARG
+    assert call(shape=(1, 2, 1024, 96, 64, 64)) == B.SA_ERR_UNSUPPORTED
+    # 262,144 tokens in 64-query blocks: one head's plan needs more than 128 MiB
+    one = lib.sparse_attn_plan_workspace_bytes(1, 1, 262144, 64, 64, 64)
+    assert one > 128 << 20
+    assert call(shape=(1, 1, 262144, 64, 64, 64)) == B.SA_ERR_WORKSPACE
+    # the largest workload shapes fit one head (and more) in the scratch
+    assert lib.sparse_attn_plan_workspace_bytes(1, 1, 245760, 128, 128, 64) <= 128 << 20
+    assert lib.sparse_attn_plan_workspace_bytes(1, 1, 262144, 64, 128, 64) <= 128 << 20
 
 
 def test_pipelined_validation(lib):
