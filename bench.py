@@ -115,10 +115,22 @@ def traffic_for(workload: str, launch_bytes_alg: float):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 15.0):
-    """The oracle as it stands, on a bounded sample: the mask track of one query block,
-    then the float64 output track over whole heads (0, 1, ...) until the budget is used.
-    q, k, v hold the heads the CSR (rp, ci) describes, in order."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 15.0, mask_heads=None):
+    """The oracle as it stands, on a bounded sample: the mask track (pooling, scores and
+    the hybrid selection) of heads 0 .. mask_heads-1 (all heads by default), then the
+    float64 output track over whole heads (0, 1, ...) until the budget is used. q, k, v
+    hold the heads the CSR (rp, ci) describes, in order."""
     from oracle import oracle_plan, sparse_attention
     try:
         from threadpoolctl import threadpool_info
@@ -126,9 +138,10 @@ def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 15.0):
     except Exception:
         threads = os.cpu_count() or 1
     nq = w.n_qblk
+    n_mask = q.shape[1] if mask_heads is None else min(mask_heads, q.shape[1])
     t0 = time.perf_counter()
-    oracle_plan(W.to_f32(q[:, :1]), W.to_f32(k[:, :1]), w.block_q, w.block_kv, w.topk, w.top_p,
-                rows=[(0, 0, 0)])
+    for h in range(n_mask):
+        oracle_plan(W.to_f32(q[:, h:h + 1]), W.to_f32(k[:, h:h + 1]), w.block_q, w.block_kv, w.topk, w.top_p)
     t_mask = time.perf_counter() - t0
     ksize = np.minimum(w.block_kv, w.N - np.arange(w.n_kvblk) * w.block_kv)
     done_flops, n_rows, n_heads, t_out = 0.0, 0, 0, 0.0
@@ -152,9 +165,16 @@ def cpu_baseline(w: W.Workload, q, k, v, rp, ci, budget_s: float = 15.0):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"heads 0..{n_heads - 1} of {w.name}: the float64 sparse output track over all "
-                   f"{n_rows} of their query blocks ({t_out:.1f} s); the mask track for one query block "
-                   f"took {t_mask:.2f} s (pooling of the whole head included)"),
+        "cpu_model": cpu_model(),
+        "ms_mask_track": round(1e3 * t_mask, 1),
+        "mask_track_rows": int(n_mask * nq),
+        "ms_output_track": round(1e3 * t_out, 1),
+        "output_track_rows": int(n_rows),
+        "output_track_gflops": round(done_flops / t_out / 1e9, 2),
+        "sample": (f"{w.name}: the mask track of heads 0..{n_mask - 1} ({n_mask * nq} query blocks, "
+                   f"{t_mask:.1f} s), then the float64 sparse output track of heads 0..{n_heads - 1} "
+                   f"({n_rows} query blocks, {t_out:.1f} s); value = kept-pair flops of the output "
+                   f"track per second"),
     }
 
 
@@ -241,6 +261,112 @@ def time_backward(sa, torch, w, dq, dk, dv, p, pairs, args, stream):
     }
 
 
+def other_config(sa, torch, w: W.Workload, steps: int, warmup: int, dense: bool = True) -> dict:
+    """One workload besides the headline one: the plan and the forward timed separately
+    (HIP events on the launch stream, means over `steps` calls after `warmup`), the
+    pipelined step where the headline would use it, the same forward on the all-ones plan,
+    and the realised sparsity."""
+    t0 = time.time()
+    q, k, v, alpha = W.make_inputs(w)
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    dq, dk, dv = dev(q), dev(k), dev(v)
+    del q, k, v
+    dalpha = dev(alpha) if w.linear else None
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(sa.plan_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(dq)
+    p = None
+    for _ in range(max(1, warmup)):
+        p = sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
+    torch.cuda.synchronize()
+    rp, ci = p.csr()
+    flops, pairs = kept_flops(rp, ci, w)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        p = sa.plan(dq, dk, w.block_q, w.block_kv, w.topk, w.top_p, workspace=ws)
+        e[1].record(stream)
+        sa.fwd(dq, dk, dv, p, alpha=dalpha, out=o)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_plan = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_fwd = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    t_step = t_plan + t_fwd
+    res = {"B": w.B, "H": w.H, "N": w.N, "D": w.D, "dtype": w.dtype, "block_q": w.block_q,
+           "block_kv": w.block_kv, "topk": w.topk, "top_p": w.top_p, "linear_branch": bool(w.linear),
+           "ms_plan": round(t_plan, 4), "ms_fwd": round(t_fwd, 4), "ms_step_sequential": round(t_step, 4)}
+    if w.rows >= PIPE_MIN_ROWS and not w.linear:
+        for _ in range(max(1, warmup)):
+            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=4, out=o)
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for a_, b_ in zip(e0, e1):
+            a_.record(stream)
+            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=4, out=o)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        t_step = float(np.mean([a_.elapsed_time(b_) for a_, b_ in zip(e0, e1)]))
+        res["ms_step_pipelined"] = round(t_step, 4)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    nnz = int(rp[-1])
+    res.update({
+        "ms_step": round(t_step, 4),
+        "step_tflops": round(flops / t_step / 1e9, 2),
+        "fwd_tflops": round(flops / t_fwd / 1e9, 2),
+        "fwd_frac_of_peak": round(flops / t_fwd / 1e9 / peak, 4),
+        "peak_tflops": peak,
+        "kept_pairs": pairs,
+        "nnz_tiles": nnz,
+        "tile_sparsity": round(1.0 - nnz / float(w.rows * w.n_kvblk), 5),
+        "pair_sparsity": round(1.0 - pairs / float(w.B * w.H * w.N * w.N), 5),
+    })
+    if dense:
+        pd = sa.plan_dense(dq, w.block_q, w.block_kv)
+        sa.fwd(dq, dk, dv, pd, out=o)
+        nd = 3
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+        for a_, b_ in zip(e0, e1):
+            a_.record(stream)
+            sa.fwd(dq, dk, dv, pd, out=o)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        t_dense = float(np.mean([a_.elapsed_time(b_) for a_, b_ in zip(e0, e1)]))
+        dflops = 4.0 * w.D * w.B * w.H * float(w.N) * w.N
+        res.update({
+            "ms_dense_fwd": round(t_dense, 4),
+            "dense_tflops": round(dflops / t_dense / 1e9, 2),
+            "speedup_vs_dense": round(t_dense / t_step, 3),
+            "speedup_vs_dense_fwd_only": round(t_dense / t_fwd, 3),
+            "per_kept_tile_util_ratio": round((flops / t_fwd) / (dflops / t_dense), 4),
+        })
+        del pd
+    log(f"{w.name}: plan {t_plan:.3f} ms, fwd {t_fwd:.3f} ms ({res['fwd_tflops']} TFLOP/s), step "
+        f"{t_step:.3f} ms, tile sparsity {res['tile_sparsity']}" +
+        (f", dense {res['ms_dense_fwd']:.2f} ms" if dense else "") + f" [{time.time() - t0:.0f} s]")
+    del dq, dk, dv, o, ws, p, dalpha
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep_exponents(points) -> dict:
+    """Least-squares slopes of log(time) against log(N) over the length sweep."""
+    n = np.log([x["N"] for x in points])
+    out = {}
+    for key in ("ms_step", "ms_fwd", "ms_dense_fwd"):
+        if all(key in x for x in points):
+            out["exponent_" + key[3:]] = round(float(np.polyfit(n, np.log([x[key] for x in points]), 1)[0]), 3)
+    out["exponent_kept_pairs"] = round(float(np.polyfit(n, np.log([x["kept_pairs"] for x in points]), 1)[0]), 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +395,9 @@ def main():
                          "int8: the quantiser and the attention kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (by default the other workloads and "
+                         "the long workload's length sweep are timed too, under 'configs')")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -491,6 +620,29 @@ def main():
         qual["pass2_tflops"] = round(2.0 * w.D * w.B * w.H * float(w.N) * w.N / t2 / 1e9, 1)
         out["quality"] = qual
         del pd, lse, tmax, tmass, hq, hk, hv
+    if not args.no_configs:
+        # every other workload (plan, forward, dense forward, sparsity), and the length
+        # sweep of the long workload with its scaling exponents
+        del raw, dq, dk, dv, o, ws
+        torch.cuda.empty_cache()
+        n_other = max(3, min(args.steps, 10))
+        configs = {}
+        for name in W.CONFIGS:
+            if name != w.name:
+                configs[name] = other_config(sa, torch, W.CONFIGS[name], n_other, args.warmup)
+        sweep = []
+        for sw in W.long_sweep():
+            if sw.N == W.LONG_245K.N:
+                ent = dict(configs.get(W.LONG_245K.name) or out)
+            else:
+                ent = other_config(sa, torch, sw, n_other, args.warmup)
+            sweep.append({"T": sw.grid[0], "N": sw.N, "ms_step": ent["ms_step"] if "ms_step" in ent
+                          else ent["ms_per_step"], "ms_fwd": ent["ms_fwd"], "ms_plan": ent["ms_plan"],
+                          "ms_dense_fwd": ent.get("ms_dense_fwd"), "kept_pairs": ent["kept_pairs"],
+                          "tile_sparsity": ent["tile_sparsity"],
+                          "speedup_vs_dense": ent.get("speedup_vs_dense")})
+        configs["long_sweep"] = {"points": sweep, **sweep_exponents(sweep)}
+        out["configs"] = configs
     if not args.no_cpu_baseline:
         if qc is not None:
             # the oracle on the same cube-ordered head 0 as the plan's CSR describes
