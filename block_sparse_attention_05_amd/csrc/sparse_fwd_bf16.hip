@@ -50,7 +50,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lbf16x4_t;
 constexpr int kVmcnt0 = 0x0F70;
 
 constexpr int kBk = 64;            // keys per tile
-constexpr float kLazy = 8.0f;      // lazy-max margin, log2 units
+constexpr float kLazy = 16.0f;      // lazy-max margin, log2 units
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   const int q = G / 8;
@@ -115,6 +115,21 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // storage row of this query's q, o and lse (positions map through the plan's table)
   int qrow = qi;
   if (a.q_order && q_ok) qrow = min(max(a.q_order[(size_t)(bh % a.H) * N + qi], 0), N - 1);
+  // loads that depend on the row alone go out before the row's CSR range comes back: the
+  // Q fragments and, with visit lists, the first two kept blocks
+  bf16x8_t qf[KSTEPS];   // Q fragments: B operand of S^T = K Q^T
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (q_ok) w = *reinterpret_cast<const uint4 *>(qg + (size_t)qrow * D + s * 16 + hf * 8);
+    qf[s] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  int vis0 = 0, vis1 = 0;
+  if (a.visit) {
+    const int32_t *vr = a.visit + (size_t)row * a.n_kvblk;
+    vis0 = vr[0];
+    if (a.n_kvblk > 1) vis1 = vr[1];
+  }
   const int beg = a.row_ptr[row];
   const int end = a.row_ptr[row + 1];
 
@@ -137,15 +152,6 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       if (a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = -INFINITY;
     }
     return;
-  }
-
-  // Q fragments: B operand of S^T = K Q^T
-  bf16x8_t qf[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (q_ok) w = *reinterpret_cast<const uint4 *>(qg + (size_t)qrow * D + s * 16 + hf * 8);
-    qf[s] = __builtin_bit_cast(bf16x8_t, w);
   }
 
   // Direct HBM -> LDS tile loads. Load i of a matrix fills LDS granules 64i .. 64i+63 of
@@ -353,14 +359,15 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // ahead of its loads and the indices one further.
   const int n = end - beg;
   const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
-  int c_next = n > 1 ? cols[1] : 0;
+  const int col0 = a.visit ? vis0 : cols[0];
+  int c_next = n > 1 ? (a.visit ? vis1 : cols[1]) : 0;
   int tab_next = 0;
   if constexpr (GATHER) {
-    issue_g(tab_load(__builtin_amdgcn_readfirstlane(cols[0])), k0s, v0s);
+    issue_g(tab_load(__builtin_amdgcn_readfirstlane(col0)), k0s, v0s);
     if (n > 1) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
     c_next = n > 2 ? cols[2] : 0;
   } else {
-    issue(cols[0], k0s, v0s);
+    issue(__builtin_amdgcn_readfirstlane(col0), k0s, v0s);
   }
   // loads of tile t + 1 into (kd, vd), and the look-ahead for later tiles
   auto next = [&](int t, char *kd, char *vd) {

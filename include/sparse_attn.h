@@ -167,8 +167,8 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_plan *plan, int with_linear);
  * natural-log sum of exp(logits) over kept tokens (-inf for an empty row).
  * workspace: sparse_attn_fwd_workspace_bytes bytes (may be NULL when that is 0).
  * Rounding: a row's tiles are taken in the plan's visit order (when it has one); for
- * bf16 without lse the running max is lazy (it may trail the true max by up to 2^8 in
- * the log2 domain), with lse it is exact. Both meet the same error bounds, but o may
+ * bf16 without lse the running max is lazy (it may trail the true max by up to 16 in
+ * the log2 domain, so probabilities reach at most 2^16), with lse it is exact. Both meet the same error bounds, but o may
  * differ in its last bits between a call with lse and one without. */
 sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype dtype,
                           int B, int H, int N, int D, const sa_plan *plan,
