@@ -163,6 +163,58 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
   *reinterpret_cast<float4 *>(o + 4) = r1;
 }
 
+// The same sums for bf16 rows in raster order (no table) with a register footprint of at
+// most 32: two rows in flight per thread and 32-bit byte offsets from one base (tensors
+// under 4 GiB). Two forward workgroups leave 32 registers per lane of a SIMD free, so
+// this kernel's waves fit beside them: the pooling of one chunk of heads runs on the
+// CUs that the previous chunk's forward occupies instead of waiting for them.
+template <int D>
+__global__ __launch_bounds__(256) void pool_lean_kernel(const uint16_t *__restrict__ x, int N, int bs,
+                                                        int nblk, long total_blocks,
+                                                        float *__restrict__ out) {
+  constexpr int kTpb = D / 8;
+  constexpr int kBlocksPerWg = 256 / kTpb;
+  constexpr int kInFlight = 2;
+  const int sub = threadIdx.x / kTpb;
+  const int lane = threadIdx.x % kTpb;
+  const long g = (long)blockIdx.x * kBlocksPerWg + sub;
+  if (g >= total_blocks) return;
+  const long bh = g / nblk;
+  const int I = (int)(g % nblk);
+  const int t0 = I * bs;
+  const int cnt = min(bs, N - t0);
+  const char *base = reinterpret_cast<const char *>(x);
+  uint32_t off = (uint32_t)((((size_t)bh * N + t0) * D + lane * 8) * 2);
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  auto add = [&](const uint4 &w) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[2 * c] = acc[2 * c] + __uint_as_float(ws[c] << 16);
+      acc[2 * c + 1] = acc[2 * c + 1] + __uint_as_float(ws[c] & 0xffff0000u);
+    }
+  };
+  int t = 0;
+  for (; t + kInFlight <= cnt; t += kInFlight) {
+    uint4 w[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) w[u] = *reinterpret_cast<const uint4 *>(base + off + u * D * 2);
+    off += kInFlight * D * 2;
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) add(w[u]);
+  }
+  for (; t < cnt; ++t) {
+    add(*reinterpret_cast<const uint4 *>(base + off));
+    off += D * 2;
+  }
+  const float fc = (float)cnt;
+  float *o = out + (size_t)g * D + lane * 8;
+  *reinterpret_cast<float4 *>(o) = make_float4(acc[0] / fc, acc[1] / fc, acc[2] / fc, acc[3] / fc);
+  *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4] / fc, acc[5] / fc, acc[6] / fc, acc[7] / fc);
+}
+
 // ---------------------------------------------------------------- scores
 // S[bh, I, J] for a 64 x 64 tile per workgroup; each thread owns a 4 x 4 patch and keeps
 // one running sum per output, adding the rounded products in ascending d.
@@ -791,7 +843,13 @@ hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int H, int N, int D, 
   const unsigned grid = (unsigned)((total + per_wg - 1) / per_wg);
 #define SA_POOL(T, DD, O)                                                                       \
   pool_kernel<T, DD, O><<<grid, 256, 0, s>>>((const T *)x, H, N, bs, nblk, total, order, out)
-  if (dt == SA_BF16) {
+  const bool lean = order == nullptr && (size_t)BH * N * D * 2 < ((size_t)1 << 32);
+  if (dt == SA_BF16 && lean) {
+    if (D == 128)
+      pool_lean_kernel<128><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);
+    else
+      pool_lean_kernel<64><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);
+  } else if (dt == SA_BF16) {
     if (D == 128) {
       if (order) SA_POOL(uint16_t, 128, true); else SA_POOL(uint16_t, 128, false);
     } else {
