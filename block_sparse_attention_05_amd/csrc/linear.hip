@@ -44,12 +44,11 @@ __device__ __forceinline__ float bf(uint32_t w, int hi) {
   return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
 }
 __device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
-__device__ __forceinline__ uint32_t rne_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// two floats to packed bf16, rounded to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return rne_bf16(a) | (rne_bf16(b) << 16); }
 
 // phi of 8 bf16 values packed in a uint4, re-rounded to bf16
 __device__ __forceinline__ uint4 phi8(uint4 w) {
