@@ -82,8 +82,13 @@ __device__ __forceinline__ void store_t4x8(uint16_t *dst, int ld, const uint4 (&
 // ---------------------------------------------------------------- prepass
 // grid (chunks, B*H), 256 threads. Wave w owns the (c-block, d-block) pairs
 // p = w, w+4, ... of the (D/32)^2 32x32 blocks of H.
+// Staging: thread c < 16 * D / 8 owns token group rg = c % 16 (4 tokens) and channels
+// 8 * (c / 16) .. +7 of every tile, so a wave's transposed 8-byte stores cover 16 token
+// groups and both parities of the channel octet: with 36-dword rows each store lands on
+// all 64 banks twice, the least a 512-byte store can take. The thread also keeps its
+// channels' phi(k) sums over the chunk; they are added across token groups at the end.
 template <int D>
-__global__ __launch_bounds__(256) void linear_kv_kernel(const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void linear_kv_kernel(const uint16_t *__restrict__ k,
                                                         const uint16_t *__restrict__ v, int N,
                                                         float *__restrict__ partial,
                                                         uint16_t *__restrict__ phik, int n_pad) {
@@ -103,17 +108,21 @@ __global__ __launch_bounds__(256) void linear_kv_kernel(const uint16_t *__restri
   const int t_beg = chunk * kChunk;
   const int t_end = min(N, t_beg + kChunk);
 
+  static_assert(CHUNKS_T <= 256, "one staging slot per thread");
   floatx16 acc[PER_WAVE];
 #pragma unroll
   for (int p = 0; p < PER_WAVE; ++p)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[p][i] = 0.0f;
-  float zacc = 0.0f;  // thread tid < D: sum of phi(k)[tid] over the chunk
+  const bool stager = tid < CHUNKS_T;
+  const int rg = tid % (kTile / 4), col = (tid / (kTile / 4)) * 8;
+  float zp[8];  // this thread's phi(k) sums over its token groups, channels col..col+7
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zp[i] = 0.0f;
 
   for (int t0 = t_beg; t0 < t_end; t0 += kTile) {
     __syncthreads();
-    for (int c = tid; c < CHUNKS_T; c += 256) {
-      const int rg = c / (D / 8), col = (c % (D / 8)) * 8;
+    if (stager) {
       uint4 kr[4], vr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -127,16 +136,15 @@ __global__ __launch_bounds__(256) void linear_kv_kernel(const uint16_t *__restri
         }
         // t0 + 64 <= n_pad, so the pad rows past N are written here as zeros
         *reinterpret_cast<uint4 *>(pk + (size_t)tok * D + col) = kr[r];
+        zp[0] += bf(kr[r].x, 0); zp[1] += bf(kr[r].x, 1);
+        zp[2] += bf(kr[r].y, 0); zp[3] += bf(kr[r].y, 1);
+        zp[4] += bf(kr[r].z, 0); zp[5] += bf(kr[r].z, 1);
+        zp[6] += bf(kr[r].w, 0); zp[7] += bf(kr[r].w, 1);
       }
       store_t4x8(&kt[col * ROW + rg * 4], ROW, kr);
       store_t4x8(&vt[col * ROW + rg * 4], ROW, vr);
     }
     __syncthreads();
-    if (tid < D) {
-      const uint16_t *row = &kt[tid * ROW];
-#pragma unroll 8
-      for (int j = 0; j < kTile; ++j) zacc += __uint_as_float(((uint32_t)row[j]) << 16);
-    }
 #pragma unroll
     for (int p = 0; p < PER_WAVE; ++p) {
       const int blk = wid + 4 * p;
@@ -167,7 +175,19 @@ __global__ __launch_bounds__(256) void linear_kv_kernel(const uint16_t *__restri
       }
     }
   }
-  if (tid < D) out[D * D + tid] = zacc;
+  // z: the token groups' sums of each channel, added in token-group order
+  __syncthreads();
+  float *zs = reinterpret_cast<float *>(kt);  // [kTile / 4][D], 8 KB of the 18 KB tile
+  if (stager)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zs[rg * D + col + i] = zp[i];
+  __syncthreads();
+  if (tid < D) {
+    float zacc = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kTile / 4; ++g) zacc += zs[g * D + tid];
+    out[D * D + tid] = zacc;
+  }
 }
 
 // Sums the chunk partials in chunk order into H and z (fp32).
