@@ -224,13 +224,39 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Workgroup barrier for LDS written by the waves' own waited-for loads: no fence, so no
+// wait for the loads still in flight into other buffers; the clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Waits until at most n (<= O) of the stages issued after the one being waited for are
+// still in flight; each stage is LPS direct loads per wave, and loads complete in order.
+template <int LPS, int O>
+__device__ __forceinline__ void wait_stages(int n) {
+  static_assert(O * LPS < 16, "vmcnt field");
+  if constexpr (O == 0) {
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  } else {
+    if (n >= O)
+      __builtin_amdgcn_s_waitcnt(kVmcnt0 | (O * LPS));
+    else
+      wait_stages<LPS, O - 1>(n);
+  }
+}
+
+#ifndef LIN_SK
+#define LIN_SK 32
+#endif
+
 // One workgroup of four waves per query block (CSR row); QG = block_q / 32 query groups.
 // The four waves split the (D/32)^2 blocks of the row's running sum H_S[c][d] in a 2x2
 // grid: wave w takes c-blocks of half w >> 1 and d-blocks of half w & 1. phi(K) and V
 // tiles go from HBM straight into LDS, both with their 64-byte row segments XOR-swizzled
 // by row, and both MFMA operands come from transposing LDS reads (8 keys of one channel
-// per lane). At the end the waves stage H_C^T (bf16) in LDS and each wave multiplies it
-// by the phi(Q) of its query group.
+// per lane). The tiles stream through NST stages of SK keys each, NST - 1 of them in
+// flight while one is multiplied: the step is bound by the latency of L2 misses, so the
+// bytes in flight per workgroup set its rate. At the end the waves stage H_C^T (bf16) in
+// LDS and each wave multiplies it by the phi(Q) of its query group.
 template <int D, int QG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
@@ -238,8 +264,14 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   constexpr int BQ = 32 * QG;
   constexpr int VROWB = D * 2;              // bytes per tile row (unpadded)
   constexpr int TB = kTile * VROWB;         // bytes per tile
-  constexpr int VNI = D / 8;                // 1 KB direct loads per tile
-  constexpr int VNIW = (VNI + NW - 1) / NW;
+  constexpr int SK = D == 128 ? LIN_SK : 32; // keys per pipeline stage
+  constexpr int SPT = kTile / SK;           // stages per tile
+  constexpr int NST = 2 * SPT;              // stages held in LDS (4 * TB bytes in all)
+  constexpr int SB = SK * VROWB;            // bytes per tensor per stage
+  constexpr int VNIS = SB / 1024;           // 1 KB direct loads per tensor per stage
+  constexpr int VNIWS = VNIS / NW;          // ... per wave
+  constexpr int LPS = 2 * VNIWS;            // direct loads per wave per stage
+  static_assert(SK % 16 == 0 && kTile % SK == 0 && VNIS % NW == 0 && VNIWS >= 1, "stage shape");
   constexpr int VSEG = D / 32;              // 64-byte segments per row (swizzle range)
   constexpr int CB = D / 32;                // 32-channel blocks
   constexpr int WC = CB / 2;                // c-blocks per wave
@@ -250,10 +282,24 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   constexpr int kMaxList = kMaxKvBlocks / 2;
   static_assert(WC >= 1 && DBW >= 1, "shape");
 
-  __shared__ __align__(16) char k0s[TB];
-  __shared__ __align__(16) char v0s[TB];
-  __shared__ __align__(16) char k1s[TB];
-  __shared__ __align__(16) char v1s[TB];
+  // Stage buffers (phi(K) rows, then V rows), one LDS object each: the compiler then tells
+  // a stage's direct loads from the reads of another stage, and the loop's own waits
+  // decide how many stages stay in flight.
+  __shared__ __align__(16) char sb0[2 * SB], sb1[2 * SB], sb2[2 * SB], sb3[2 * SB];
+  __shared__ __align__(16) char sb4[2 * SB], sb5[2 * SB], sb6[2 * SB], sb7[2 * SB];
+  auto bufs = [&](int b) -> char * {
+    switch (b) {
+      case 0: return sb0;
+      case 1: return sb1;
+      case 2: return sb2;
+      case 3: return sb3;
+      case 4: return sb4;
+      case 5: return sb5;
+      case 6: return sb6;
+      default: return sb7;
+    }
+  };
+  static_assert(NST <= 8, "stage buffers");
   __shared__ int tiles[kMaxList];                    // the tile list of this row
   __shared__ uint32_t keptbits[kMaxKvBlocks / 32];
   __shared__ float zs[2 * D];                        // z partials, then z_C
@@ -329,46 +375,45 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   }
   __syncthreads();
 
-  // Direct loads: LDS granule (row r, physical granule pg) holds logical granule
-  // pg ^ ((r mod VSEG) << 2); load i of a tile fills granules 64i .. 64i+63.
-  uint32_t goff[VNIW];
+  // Direct loads: LDS granule (row r, physical granule pg) of a stage holds logical
+  // granule pg ^ ((r mod VSEG) << 2) of key row r0 + r (r0 a multiple of 16, so the
+  // swizzle is the same as by the tile row); load i of a stage fills granules 64i .. 64i+63.
+  uint32_t goff[VNIWS];
+  int grow[VNIWS];
 #pragma unroll
-  for (int m = 0; m < VNIW; ++m) {
+  for (int m = 0; m < VNIWS; ++m) {
     const int P = 64 * (wid + m * NW) + lane;
     const int r = P / (D / 8), pg = P % (D / 8);
+    grow[m] = r;
     goff[m] = (r * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
   }
   const int ragged_blk = (N % kTile) ? (N / kTile) : -1;
 
-  auto issue = [&](int J, char *kdst, char *vdst) {
-    const char *kb = reinterpret_cast<const char *>(pk + (size_t)J * kTile * D);
-    const char *vb = reinterpret_cast<const char *>(vg + (size_t)J * kTile * D);
+  // stage st: keys r0 .. r0 + SK - 1 of tile tiles[st / SPT], r0 = SK * (st % SPT)
+  auto issue = [&](int st, char *buf) {
+    const int J = tiles[st / SPT];
+    const int r0 = SK * (st % SPT);
+    char *kdst = buf;
+    char *vdst = buf + SB;
+    const char *kb = reinterpret_cast<const char *>(pk + ((size_t)J * kTile + r0) * D);
+    const char *vb = reinterpret_cast<const char *>(vg + ((size_t)J * kTile + r0) * D);
     // phi(K) rows past N are zero pad rows of the prepass buffer
 #pragma unroll
-    for (int m = 0; m < VNIW; ++m) {
-      const int i = wid + m * NW;
-      if (i < VNI)
-        __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
-    }
+    for (int m = 0; m < VNIWS; ++m)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + (wid + m * NW) * 1024), 16, 0, 0);
     if (J != ragged_blk) {
 #pragma unroll
-      for (int m = 0; m < VNIW; ++m) {
-        const int i = wid + m * NW;
-        if (i < VNI)
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + goff[m]), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
-      }
+      for (int m = 0; m < VNIWS; ++m)
+        __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + goff[m]), (lvoid_t *)(vdst + (wid + m * NW) * 1024), 16, 0, 0);
     } else {
       // V rows past N reload the last valid row (finite; their phi(k) is zero)
-      const int last = N - 1 - J * kTile;
+      const int last = N - 1 - J * kTile - r0;   // may be negative: the whole stage is past N
 #pragma unroll
-      for (int m = 0; m < VNIW; ++m) {
-        const int i = wid + m * NW;
-        if (i < VNI) {
-          const int P = 64 * i + lane;
-          const int r = P / (D / 8), pg = P % (D / 8);
-          const uint32_t off = (min(r, last) * D + (pg ^ ((r & (VSEG - 1)) << 2)) * 8) * 2;
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + off), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
-        }
+      for (int m = 0; m < VNIWS; ++m) {
+        const int r = grow[m];
+        const int rr = r <= last ? r : last;
+        const uint32_t off = (uint32_t)(goff[m] + (rr - r) * D * 2);
+        __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + (int32_t)off), (lvoid_t *)(vdst + (wid + m * NW) * 1024), 16, 0, 0);
       }
     }
   };
@@ -396,12 +441,14 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   for (int x = 0; x < WC; ++x) zacc[x] = 0.0f;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // H_S[c][d] += sum over the tile's keys of phi(K)[key][c] V[key][d]; the MFMA reduction
+  // H_S[c][d] += sum over the stage's keys of phi(K)[key][c] V[key][d]; the MFMA reduction
   // index hf*8 + e stands for key 16s + hf*4 + e (e < 4) or 16s + 8 + hf*4 + e - 4, the
   // same for both operands.
-  auto tile = [&](const char *ks, const char *vs) {
+  auto stage = [&](int st, const char *buf) {
+    const char *ks = buf;
+    const char *vs = buf + SB;
 #pragma unroll
-    for (int s = 0; s < kTile / 16; ++s) {
+    for (int s = 0; s < SK / 16; ++s) {
       const int base = 16 * s * VROWB;
       bf16x8_t av[WC], bv[WD];
 #pragma unroll
@@ -419,7 +466,7 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
         bv[y] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       // the two waves sharing a c-half split the z sum by k-step parity
-      if ((s & 1) == dp) {
+      if (((st * (SK / 16) + s) & 1) == dp) {
 #pragma unroll
         for (int x = 0; x < WC; ++x)
 #pragma unroll
@@ -436,18 +483,21 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
     }
   };
 
-  if (ntiles > 0) {
-    issue(tiles[0], k0s, v0s);
-    for (int it = 0; it < ntiles; it += 2) {
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();
-      if (it + 1 < ntiles) issue(tiles[it + 1], k1s, v1s);
-      tile(k0s, v0s);
-      if (it + 1 >= ntiles) break;
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();
-      if (it + 2 < ntiles) issue(tiles[it + 2], k0s, v0s);
-      tile(k1s, v1s);
+  // Stage st is multiplied from buffer st % NST; after the barrier of step st every wave
+  // is done with buffer (st - 1) % NST, which then takes stage st + NST - 1.
+  const int nst = ntiles * SPT;
+#pragma unroll
+  for (int b = 0; b < NST - 1; ++b)
+    if (b < nst) issue(b, bufs(b));
+  for (int st0 = 0; st0 < nst; st0 += NST) {
+#pragma unroll
+    for (int b = 0; b < NST; ++b) {
+      const int st = st0 + b;
+      if (st >= nst) break;
+      wait_stages<LPS, NST - 2>(min(nst - 1 - st, NST - 2));
+      lds_barrier();
+      if (st + NST - 1 < nst) issue(st + NST - 1, bufs((b + NST - 1) % NST));
+      stage(st, bufs(b));
     }
   }
 
@@ -470,15 +520,17 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
         const int d = (dp * WD + y) * 32 + l32;
         hc[x][y][i] = subtract ? hg[(size_t)c * D + d] - hacc[x][y][i] : hacc[x][y][i];
       }
-  __syncthreads();  // every wave is done with the tile buffers
-  // staged H_C^T: row d (64 rows per buffer, k0s then v0s), 16-byte granule c/8 at
+  __syncthreads();  // every wave is done with the stage buffers
+  // staged H_C^T: row d in the stage buffers (2 * SK rows each), 16-byte granule c/8 at
   // physical granule (c/8) ^ (d mod HG)
+  constexpr int RPB = 2 * SK;
+  static_assert(D % RPB == 0 && D / RPB <= NST, "H_C^T fits in the stage buffers");
 #pragma unroll
   for (int x = 0; x < WC; ++x)
 #pragma unroll
     for (int y = 0; y < WD; ++y) {
       const int d = (dp * WD + y) * 32 + l32;
-      char *hrow = (d < 64 ? k0s : v0s) + (d & 63) * VROWB;
+      char *hrow = bufs(d / RPB) + (d % RPB) * VROWB;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int gr = (cp * WC + x) * 4 + q4;
@@ -511,7 +563,7 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
 #pragma unroll
   for (int t = 0; t < DBW; ++t) {
     const int d = (dstart + t) * 32 + l32;
-    const char *hrow = (d < 64 ? k0s : v0s) + (d & 63) * VROWB;
+    const char *hrow = bufs(d / RPB) + (d % RPB) * VROWB;
     floatx16 oacc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[i] = 0.0f;

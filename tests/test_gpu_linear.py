@@ -129,3 +129,38 @@ def test_sparse_linear_workload_sampled():
         want.append(blend(os_[(b, h, I)][0], ol[(b, h, I)], ent["alpha"], h=h))
     mx, rr = check_out(np.concatenate(got), np.concatenate(want), "bf16", w.name)
     log(f"{w.name}: sampled {len(rows)} rows max|dO| {mx:.2e} rel-RMS {rr:.2e}")
+
+
+@pytest.mark.parametrize("D,tail", [(128, 47), (128, 17), (64, 17)])
+def test_linear_tile_counts(D, tail):
+    """Rows whose tile lists (kept tiles, or the complement when more than half is kept)
+    hold 1 to 5 tiles, with the ragged last KV block (tail tokens: more, or fewer, than
+    half a block) inside some of them: every fill level of the apply step's load pipeline,
+    and its tail, against the oracle's Ol (alpha = 0)."""
+    w = small(f"lin_counts_d{D}_t{tail}", 1, 64 * 19 + tail, D, 128, 0.1, 0.9)
+    ent = inputs(w)
+    vb, dv = offset_v(ent, 0.9)
+    nq, nkv = w.n_qblk, w.n_kvblk
+    assert nq == 10 and nkv == 20
+    rng = np.random.default_rng(23)
+    rows = []
+    for r in range(nq):
+        n = r % 5 + 1 if r < 5 else r - 4                  # tiles in the row's list
+        with_last = r % 2 == 0                               # the ragged block among them
+        pool = np.arange(nkv - 1)
+        pick = list(rng.choice(pool, n - 1 if with_last else n, replace=False))
+        if with_last:
+            pick.append(nkv - 1)
+        if r < 5:                                            # kept tiles, summed and subtracted
+            rows.append(np.sort(np.array(pick)))
+        else:                                                # complement summed directly
+            rows.append(np.setdiff1d(np.arange(nkv), pick))
+    rp = np.zeros(nq + 1, np.int64)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    ci = np.concatenate(rows).astype(np.int32)
+    p = sa.plan_from_csr(ent["dq"], rp, ci, w.block_q, w.block_kv)
+    a0 = torch.zeros((w.H, w.D), dtype=torch.float32, device="cuda")
+    o = to_f64(sa.fwd(ent["dq"], ent["dk"], dv, p, alpha=a0))
+    ol = linear_branch(ent["q32"], ent["k32"], W.to_f32(vb), rp, ci, w.block_q, w.block_kv)
+    mx, rr = check_out(o, ol, "bf16", w.name + " Ol")
+    log(f"{w.name}: Ol max|d| {mx:.2e} rel-RMS {rr:.2e}")
