@@ -99,15 +99,16 @@ void fill_plan(sa_plan *p, const Shape &s, int dt, char *ws, const PlanLayout &L
 
 sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
 
-// Linear-branch workspace: per head H^T (bf16 [D, D]) and z (fp32 [D]), the per-chunk
-// partials of both (fp32), and the fp32 linear output Ol [B, H, N, D].
+// Linear-branch workspace: per head H (fp32 [D, D]) and z (fp32 [D]), the per-chunk
+// partials of both (fp32), phi(K) (bf16, padded to whole KV blocks), and per plan row the
+// masked-out sums H_C^T (bf16 [D, D]) and z_C (fp32 [D]).
 struct FwdLayout {
-  size_t lin_h, lin_z, partial, ol, phik, total;
+  size_t lin_h, lin_z, partial, hct, zc, phik, total;
   int chunks, n_pad;
 };
 
 FwdLayout fwd_layout(const Shape &s, int with_linear) {
-  FwdLayout L{0, 0, 0, 0, 0, 0, 0, 0};
+  FwdLayout L{0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (!with_linear) return L;
   const size_t BH = (size_t)s.B * s.H;
   L.chunks = linear_prepass_chunks(s.N);
@@ -121,7 +122,8 @@ FwdLayout fwd_layout(const Shape &s, int with_linear) {
   L.lin_h = take(BH * s.D * s.D * 4);
   L.lin_z = take(BH * s.D * 4);
   L.partial = take(BH * (size_t)L.chunks * s.D * (s.D + 1) * 4);
-  L.ol = take(BH * (size_t)s.N * s.D * 4);
+  L.hct = take((size_t)s.R * s.D * s.D * 2);
+  L.zc = take((size_t)s.R * s.D * 4);
   L.phik = take(BH * (size_t)L.n_pad * s.D * 2);
   L.total = off;
   return L;
@@ -323,7 +325,8 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   a.scale_log2_f64 = 1.4426950408889634 / sqrt((double)D);
   a.alpha = nullptr;
-  a.ol = nullptr;
+  a.hct = nullptr;
+  a.zc = nullptr;
   if (alpha != nullptr) {
     char *ws = static_cast<char *>(workspace);
     LinearBufs lb;
@@ -333,12 +336,14 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
     lb.n_pad = L.n_pad;
     lb.h = reinterpret_cast<float *>(ws + L.lin_h);
     lb.z = reinterpret_cast<float *>(ws + L.lin_z);
-    lb.ol = reinterpret_cast<float *>(ws + L.ol);
+    lb.hct = reinterpret_cast<uint16_t *>(ws + L.hct);
+    lb.zc = reinterpret_cast<float *>(ws + L.zc);
     hipError_t e = launch_linear_prepass(k, v, dtype, B * H, N, D, lb, stream);
     if (e == hipSuccess) e = launch_linear_apply(a, lb, stream);
     if (e != hipSuccess) return SA_ERR_HIP;
     a.alpha = alpha;
-    a.ol = lb.ol;
+    a.hct = lb.hct;
+    a.zc = lb.zc;
   }
   return hip_status(launch_fwd(a, dtype, stream));
 }

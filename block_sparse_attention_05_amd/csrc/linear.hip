@@ -6,8 +6,7 @@
 //   Ol_i = phi(q_i)^T H_C / phi(q_i)^T z_C,  H_C = sum_{j in C_I} phi(k_j) v_j^T,
 //                                           z_C = sum_{j in C_I} phi(k_j).
 // H_C is a D x D matrix shared by the whole query block, so the apply step forms it once
-// per block and multiplies it by the block's phi(Q): the per-tile work is one D x D x 64
-// product instead of two BQ x 64 x D ones.
+// per block: the per-tile work is one D x D x 64 product instead of two BQ x 64 x D ones.
 //   linear_kv_kernel     per (head, token chunk): partial H and z with bf16 MFMA and fp32
 //                        accumulation; also writes phi(K) in bf16 with zero pad rows;
 //   linear_reduce_kernel sums the chunk partials in chunk order (deterministic) into the
@@ -16,9 +15,11 @@
 //                        H_C and z_C are the totals minus the kept tiles' sums (formed in
 //                        fp32, then rounded once); otherwise the complement tiles are
 //                        summed directly, so no sum is formed as a small difference of
-//                        large ones. A query block that keeps every KV block gets Ol = 0.
-//                        Ol is written in fp32 for the blend O = alpha*Os + (1 - alpha)*Ol
-//                        in the attention epilogue.
+//                        large ones. It writes H_C^T in bf16 and z_C in fp32 per block; a
+//                        block that keeps every KV block writes nothing (Ol = 0).
+// The forward kernel's epilogue then forms Ol = phi(Q) H_C / phi(Q) z_C on MFMA from the
+// Q fragments it already holds and blends O = alpha*Os + (1 - alpha)*Ol, so Ol never goes
+// through memory.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -248,20 +249,18 @@ __device__ __forceinline__ void wait_stages(int n) {
 #define LIN_SK 32
 #endif
 
-// One workgroup of four waves per query block (CSR row); QG = block_q / 32 query groups.
-// The four waves split the (D/32)^2 blocks of the row's running sum H_S[c][d] in a 2x2
-// grid: wave w takes c-blocks of half w >> 1 and d-blocks of half w & 1. phi(K) and V
-// tiles go from HBM straight into LDS, both with their 64-byte row segments XOR-swizzled
-// by row, and both MFMA operands come from transposing LDS reads (8 keys of one channel
-// per lane). The tiles stream through NST stages of SK keys each, NST - 1 of them in
-// flight while one is multiplied: the step is bound by the latency of L2 misses, so the
-// bytes in flight per workgroup set its rate. At the end the waves stage H_C^T (bf16) in
-// LDS and each wave multiplies it by the phi(Q) of its query group.
-template <int D, int QG>
+// One workgroup of four waves per query block (CSR row). The four waves split the
+// (D/32)^2 blocks of the row's running sum H_S[c][d] in a 2x2 grid: wave w takes c-blocks
+// of half w >> 1 and d-blocks of half w & 1. phi(K) and V tiles go from HBM straight into
+// LDS, both with their 64-byte row segments XOR-swizzled by row, and both MFMA operands
+// come from transposing LDS reads (8 keys of one channel per lane). The tiles stream
+// through NST stages of SK keys each, NST - 1 of them in flight while one is multiplied.
+// At the end the waves round H_C^T to bf16, stage it in LDS and write it out in row order
+// with z_C; the forward's epilogue multiplies it by phi(q).
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   constexpr int NW = 4;
-  constexpr int BQ = 32 * QG;
   constexpr int VROWB = D * 2;              // bytes per tile row (unpadded)
   constexpr int TB = kTile * VROWB;         // bytes per tile
   constexpr int SK = D == 128 ? LIN_SK : 32; // keys per pipeline stage
@@ -276,11 +275,9 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   constexpr int CB = D / 32;                // 32-channel blocks
   constexpr int WC = CB / 2;                // c-blocks per wave
   constexpr int WD = CB / 2;                // d-blocks per wave
-  constexpr int KSTEPS = D / 16;
   constexpr int HG = D / 8;                 // 16-byte granules per staged H_C^T row
-  constexpr int DBW = CB * QG / NW;         // d-blocks per wave in the final product
   constexpr int kMaxList = kMaxKvBlocks / 2;
-  static_assert(WC >= 1 && DBW >= 1, "shape");
+  static_assert(WC >= 1, "shape");
 
   // Stage buffers (phi(K) rows, then V rows), one LDS object each: the compiler then tells
   // a stage's direct loads from the reads of another stage, and the loop's own waits
@@ -315,36 +312,14 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   const int row = xcd_remap(blockIdx.x, gridDim.x);
   const int nQ = a.n_qblk, nKV = a.n_kvblk, N = a.N;
   const int bh = row / nQ;
-  const int I = row - bh * nQ;
   const size_t head = (size_t)bh * N * D;
-  const uint16_t *qg = reinterpret_cast<const uint16_t *>(a.q) + head;
   const uint16_t *vg = reinterpret_cast<const uint16_t *>(a.v) + head;
   const uint16_t *pk = lb.phik + (size_t)bh * lb.n_pad * D;
-  float *olg = lb.ol + head;
 
   const int beg = a.row_ptr[row], end = a.row_ptr[row + 1];
   const int kept = end - beg;
-  if (kept == nKV) {  // empty complement: Ol = 0
-    for (int e = tid * 4; e < BQ * D; e += NW * 64 * 4) {
-      const int qi = I * BQ + e / D;
-      if (qi < N) *reinterpret_cast<float4 *>(olg + (size_t)qi * D + e % D) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    return;
-  }
+  if (kept == nKV) return;  // empty complement: the forward takes Ol = 0 without reading
   const bool subtract = kept <= nKV / 2;
-
-  // raw q of this wave's final-product query group, loaded early
-  const int g = wid % QG;
-  const int qi = I * BQ + g * 32 + l32;   // query position (Ol is written by position)
-  const bool q_ok = qi < N;
-  int qrow = qi;                          // storage row of q
-  if (a.q_order && q_ok) qrow = min(max(a.q_order[(size_t)(bh % a.H) * N + qi], 0), N - 1);
-  uint4 qraw[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    qraw[s] = make_uint4(0, 0, 0, 0);
-    if (q_ok) qraw[s] = *reinterpret_cast<const uint4 *>(qg + (size_t)qrow * D + s * 16 + hf * 8);
-  }
 
   // tile list: the kept tiles (subtract) or the complement (direct sum); both fit in
   // nKV / 2 entries
@@ -539,49 +514,16 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
       }
     }
   __syncthreads();
+  // H_C^T out to the row's slot, 16-byte granules in order (coalesced), and z_C
+  uint16_t *hco = lb.hct + (size_t)row * D * D;
+  for (int G = tid; G < D * HG; G += NW * 64) {
+    const int d = G / HG, gr = G % HG;
+    const uint4 w = *reinterpret_cast<const uint4 *>(bufs(d / RPB) + (d % RPB) * VROWB + ((gr ^ (d & (HG - 1))) * 16));
+    *reinterpret_cast<uint4 *>(hco + (size_t)d * D + gr * 8) = w;
+  }
   if (tid < D) {
     const float zsum = zs[tid] + zs[D + tid];
-    zs[tid] = subtract ? lb.z[(size_t)bh * D + tid] - zsum : zsum;
-  }
-  __syncthreads();
-
-  // Ol^T[d][q] = sum_c H_C^T[d][c] phi(q)[c] / (phi(q) . z_C)
-  bf16x8_t pf[KSTEPS];
-  float zdot = 0.0f;
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    const uint4 w = q_ok ? phi8(qraw[s]) : make_uint4(0, 0, 0, 0);
-    pf[s] = __builtin_bit_cast(bf16x8_t, w);
-    const float4 z0 = *reinterpret_cast<const float4 *>(&zs[s * 16 + hf * 8]);
-    const float4 z1 = *reinterpret_cast<const float4 *>(&zs[s * 16 + hf * 8 + 4]);
-    zdot += bf(w.x, 0) * z0.x + bf(w.x, 1) * z0.y + bf(w.y, 0) * z0.z + bf(w.y, 1) * z0.w +
-            bf(w.z, 0) * z1.x + bf(w.z, 1) * z1.y + bf(w.w, 0) * z1.z + bf(w.w, 1) * z1.w;
-  }
-  const float den = zdot + __shfl_xor(zdot, 32);
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  const int dstart = (wid / QG) * DBW;
-#pragma unroll
-  for (int t = 0; t < DBW; ++t) {
-    const int d = (dstart + t) * 32 + l32;
-    const char *hrow = bufs(d / RPB) + (d % RPB) * VROWB;
-    floatx16 oacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[i] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(hrow + (((2 * s + hf) ^ (d & (HG - 1))) * 16));
-      oacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf[s], oacc, 0, 0, 0);
-    }
-    if (q_ok) {
-      float *orow = olg + (size_t)qi * D;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dd = (dstart + t) * 32 + g4 * 8 + hf * 4;
-        *reinterpret_cast<float4 *>(orow + dd) =
-            make_float4(oacc[g4 * 4 + 0] * inv, oacc[g4 * 4 + 1] * inv, oacc[g4 * 4 + 2] * inv,
-                        oacc[g4 * 4 + 3] * inv);
-      }
-    }
+    lb.zc[(size_t)row * D + tid] = subtract ? lb.z[(size_t)bh * D + tid] - zsum : zsum;
   }
 }
 
@@ -608,17 +550,10 @@ hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int 
 
 hipError_t launch_linear_apply(const FwdArgs &a, const LinearBufs &lb, hipStream_t s) {
   const int R = a.B * a.H * a.n_qblk;
-  if (a.D == 128) {
-    if (a.block_q == 128)
-      linear_apply_kernel<128, 4><<<R, 256, 0, s>>>(a, lb);
-    else
-      linear_apply_kernel<128, 2><<<R, 256, 0, s>>>(a, lb);
-  } else {
-    if (a.block_q == 128)
-      linear_apply_kernel<64, 4><<<R, 256, 0, s>>>(a, lb);
-    else
-      linear_apply_kernel<64, 2><<<R, 256, 0, s>>>(a, lb);
-  }
+  if (a.D == 128)
+    linear_apply_kernel<128><<<R, 256, 0, s>>>(a, lb);
+  else
+    linear_apply_kernel<64><<<R, 256, 0, s>>>(a, lb);
   return hipGetLastError();
 }
 

@@ -843,7 +843,12 @@ hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int H, int N, int D, 
   const unsigned grid = (unsigned)((total + per_wg - 1) / per_wg);
 #define SA_POOL(T, DD, O)                                                                       \
   pool_kernel<T, DD, O><<<grid, 256, 0, s>>>((const T *)x, H, N, bs, nblk, total, order, out)
-  const bool lean = order == nullptr && (size_t)BH * N * D * 2 < ((size_t)1 << 32);
+  // The lean kernel keeps two rows in flight per thread: with fewer than about three
+  // workgroups per CU that leaves too few bytes in flight (on the 12-head 32,760-token
+  // shape, 192 and 384 workgroups, it takes 30 us a launch against 19), with more it is
+  // as fast as the wide one and also fits beside the forward.
+  constexpr unsigned kLeanMinGrid = 3 * 256;
+  const bool lean = order == nullptr && (size_t)BH * N * D * 2 < ((size_t)1 << 32) && grid >= kLeanMinGrid;
   if (dt == SA_BF16 && lean) {
     if (D == 128)
       pool_lean_kernel<128><<<grid, 256, 0, s>>>((const uint16_t *)x, N, bs, nblk, total, out);

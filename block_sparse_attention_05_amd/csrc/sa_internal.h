@@ -45,14 +45,17 @@ struct FwdArgs {
   double scale_log2_f64;   // the same in fp64
   // linear branch (null alpha: off)
   const float *alpha;      // [H, D]
-  const float *ol;         // [B, H, N, D] fp32 linear-branch output Ol
+  const uint16_t *hct;     // [R, D, D] bf16 per plan row: H_C^T, row d = value channel
+  const float *zc;         // [R, D] fp32 per plan row: z_C
 };
 hipError_t launch_fwd(const FwdArgs &a, sa_dtype dt, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);  // sparse_fwd_bf16.hip
 // Linear branch (linear.hip). The prepass writes, per head, phi(k) in bf16 with zero rows
 // padding N up to a multiple of 64 ([B*H, n_pad, D]), H = sum_j phi(k_j) v_j^T (fp32
 // [B*H, D, D], row c = key channel, column d = value channel) and z = sum_j phi(k_j) (fp32
-// [B*H, D]); the apply step then writes Ol per query block over its masked-out blocks.
+// [B*H, D]); the apply step then writes, per query block (plan row) that does not keep
+// every KV block, the sums over its masked-out blocks: H_C^T in bf16 and z_C in fp32. The
+// forward's epilogue multiplies them by phi(q) and blends.
 struct LinearBufs {
   float *partial;          // [B*H, chunks, D*D + D] per-chunk partial H and z
   int chunks;
@@ -60,7 +63,8 @@ struct LinearBufs {
   int n_pad;
   float *h;                // [B*H, D, D]
   float *z;                // [B*H, D]
-  float *ol;               // [B*H, N, D]
+  uint16_t *hct;           // [R, D, D]
+  float *zc;               // [R, D]
 };
 hipError_t launch_linear_prepass(const void *k, const void *v, sa_dtype dt, int BH, int N, int D,
                                  const LinearBufs &lb, hipStream_t s);

@@ -67,6 +67,15 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// elu + 1 on the raw bf16 value, the linear branch's feature map
+__device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t phi2(uint32_t w) {
+  const bf16x2_t v = {(__bf16)phi(bf_lo(w)), (__bf16)phi(bf_hi(w))};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Two waves per SIMD with four-wave workgroups (two workgroups per CU by LDS). With
 // 64-query workgroups (NW = 2) the double-buffered K/V tiles still take 67.6 KB, so LDS
 // allows two workgroups, one wave per SIMD, and the register budget is not the limit.
@@ -133,22 +142,12 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   const int beg = a.row_ptr[row];
   const int end = a.row_ptr[row + 1];
 
-  if (beg == end) {
-    // no kept tile: Os = 0 (so O = (1 - alpha) * Ol with the linear branch), LSE = -inf
+  if (!LIN && beg == end) {
+    // no kept tile: O = 0, LSE = -inf (with the linear branch such a row runs the
+    // epilogue below with Os = 0, so O = (1 - alpha) * Ol)
     if (q_ok) {
-      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4) {
-        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-        if constexpr (LIN) {
-          const int h = bh % a.H;
-          const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)h * D + d);
-          const float4 lv = *reinterpret_cast<const float4 *>(a.ol + head + (size_t)qi * D + d);
-          o0 = (1.f - al.x) * lv.x;
-          o1 = (1.f - al.y) * lv.y;
-          o2 = (1.f - al.z) * lv.z;
-          o3 = (1.f - al.w) * lv.w;
-        }
-        *reinterpret_cast<uint2 *>(og + (size_t)qrow * D + d) = pack4(o0, o1, o2, o3);
-      }
+      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); d += 4)
+        *reinterpret_cast<uint2 *>(og + (size_t)qrow * D + d) = make_uint2(0u, 0u);
       if (a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = -INFINITY;
     }
     return;
@@ -358,80 +357,164 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // on a memory round trip. With GATHER the table entries of a tile are fetched one tile
   // ahead of its loads and the indices one further.
   const int n = end - beg;
-  const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
-  const int col0 = a.visit ? vis0 : cols[0];
-  int c_next = n > 1 ? (a.visit ? vis1 : cols[1]) : 0;
-  int tab_next = 0;
-  if constexpr (GATHER) {
-    issue_g(tab_load(__builtin_amdgcn_readfirstlane(col0)), k0s, v0s);
-    if (n > 1) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
-    c_next = n > 2 ? cols[2] : 0;
-  } else {
-    issue(__builtin_amdgcn_readfirstlane(col0), k0s, v0s);
-  }
-  // loads of tile t + 1 into (kd, vd), and the look-ahead for later tiles
-  auto next = [&](int t, char *kd, char *vd) {
-    if constexpr (GATHER) {
-      if (t + 1 < n) issue_g(tab_next, kd, vd);
-      if (t + 2 < n) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
-      if (t + 3 < n) c_next = cols[t + 3];
-    } else {
-      if (t + 1 < n) issue(__builtin_amdgcn_readfirstlane(c_next), kd, vd);
-      if (t + 2 < n) c_next = cols[t + 2];
+  // Linear branch: the row's H_C^T (bf16 [D][D], row d = value channel) goes by direct
+  // loads into the K/V buffers that the last tile does not use, while that tile computes:
+  // rows 0..63 into the V buffer and the rest into the K buffer, 256-byte (2D) rows with
+  // the 16-byte granule g of row d at g ^ (d mod D/8). A row that keeps every KV block
+  // has an empty complement and Ol = 0.
+  const bool lin_on = LIN && n < a.n_kvblk;
+  constexpr int HG = D / 8;                   // 16-byte granules per H_C^T row
+  constexpr int HLW = (D * D / 512) / NW;     // 1 KB loads per wave
+  static_assert((D * D / 512) % NW == 0 && D * D / 512 <= 2 * HG, "H_C^T fits in a K/V buffer pair");
+  auto issue_hct = [&](char *kd, char *vd) {
+    const char *hb = reinterpret_cast<const char *>(a.hct + (size_t)row * D * D);
+#pragma unroll
+    for (int m = 0; m < HLW; ++m) {
+      const int i = wid + m * NW;
+      const int P = 64 * i + lane;
+      const int r = P / HG, pg = P % HG;
+      const uint32_t off = (r * D + (pg ^ (r & (HG - 1))) * 8) * 2;
+      char *dst = i < HG ? vd + i * 1024 : kd + (i - HG) * 1024;
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(hb + off), (lvoid_t *)dst, 16, 0, 0);
     }
   };
-  int it = 0;
-  for (; it < n_full; it += 2) {
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    next(it, k1s, v1s);
-    tile(cols[it], k0s, v0s, std::false_type{});
-    if (it + 1 >= n_full) {
-      ++it;
-      break;
+  if (LIN ? n > 0 : true) {
+    const int n_full = n - (cols[n - 1] == ragged_blk ? 1 : 0);
+    const int col0 = a.visit ? vis0 : cols[0];
+    int c_next = n > 1 ? (a.visit ? vis1 : cols[1]) : 0;
+    int tab_next = 0;
+    if constexpr (GATHER) {
+      issue_g(tab_load(__builtin_amdgcn_readfirstlane(col0)), k0s, v0s);
+      if (n > 1) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
+      c_next = n > 2 ? cols[2] : 0;
+    } else {
+      issue(__builtin_amdgcn_readfirstlane(col0), k0s, v0s);
     }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    next(it + 1, k0s, v0s);
-    tile(cols[it + 1], k1s, v1s, std::false_type{});
-  }
-  if (n_full < n) {
-    // tile n - 1 was issued into buffer (n - 1) % 2
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    if ((n - 1) % 2 == 0)
-      tile(cols[n - 1], k0s, v0s, std::true_type{});
-    else
-      tile(cols[n - 1], k1s, v1s, std::true_type{});
+    // loads of tile t + 1 into (kd, vd), and the look-ahead for later tiles; after the
+    // last tile's loads, the linear branch's H_C^T
+    auto next = [&](int t, char *kd, char *vd) {
+      if constexpr (GATHER) {
+        if (t + 1 < n) issue_g(tab_next, kd, vd);
+        if (t + 2 < n) tab_next = tab_load(__builtin_amdgcn_readfirstlane(c_next));
+        if (t + 3 < n) c_next = cols[t + 3];
+      } else {
+        if (t + 1 < n) issue(__builtin_amdgcn_readfirstlane(c_next), kd, vd);
+        if (t + 2 < n) c_next = cols[t + 2];
+      }
+      if constexpr (LIN)
+        if (lin_on && t + 1 >= n) issue_hct(kd, vd);
+    };
+    int it = 0;
+    for (; it < n_full; it += 2) {
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+      next(it, k1s, v1s);
+      tile(cols[it], k0s, v0s, std::false_type{});
+      if (it + 1 >= n_full) {
+        ++it;
+        break;
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+      next(it + 1, k0s, v0s);
+      tile(cols[it + 1], k1s, v1s, std::false_type{});
+    }
+    if (n_full < n) {
+      // tile n - 1 was issued into buffer (n - 1) % 2
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+      if ((n - 1) % 2 == 0) {
+        if constexpr (LIN)
+          if (lin_on) issue_hct(k1s, v1s);
+        tile(cols[n - 1], k0s, v0s, std::true_type{});
+      } else {
+        if constexpr (LIN)
+          if (lin_on) issue_hct(k0s, v0s);
+        tile(cols[n - 1], k1s, v1s, std::true_type{});
+      }
+    }
+  } else if (lin_on) {
+    issue_hct(k0s, v0s);   // no kept tile (LIN only): Os = 0
   }
 
   // epilogue: normalise (and blend), store bf16
   const float l_run = lsum[0] + lsum[1];
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (q_ok) {
-    uint16_t *orow = og + (size_t)qrow * D;
+  if constexpr (!LIN) {
+    const float inv = 1.0f / l_tot;
+    if (q_ok) {
+      uint16_t *orow = og + (size_t)qrow * D;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = t * 32 + g * 8 + hf * 4;
+          *reinterpret_cast<uint2 *>(orow + d) =
+              pack4(oacc[t][g * 4 + 0] * inv, oacc[t][g * 4 + 1] * inv, oacc[t][g * 4 + 2] * inv,
+                    oacc[t][g * 4 + 3] * inv);
+        }
+      if (a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+    }
+    return;
+  }
+  const float inv = n == 0 ? 0.0f : 1.0f / l_tot;   // a row without kept tiles has Os = 0
+  // Linear branch: Ol^T[d][q] = sum_c H_C^T[d][c] phi(q)[c] / (phi(q) . z_C). phi(q)
+  // replaces the Q fragments, which are the B operand of this product as they were of
+  // S^T = K Q^T; H_C^T rows are the A operand.
+  float inv_l = 0.0f;
+  if (lin_on) {
+    const float *zc = a.zc + (size_t)row * D;
+    float zdot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      uint4 w = __builtin_bit_cast(uint4, qf[s]);
+      w.x = phi2(w.x);
+      w.y = phi2(w.y);
+      w.z = phi2(w.z);
+      w.w = phi2(w.w);
+      qf[s] = __builtin_bit_cast(bf16x8_t, w);
+      const float4 z0 = *reinterpret_cast<const float4 *>(zc + s * 16 + hf * 8);
+      const float4 z1 = *reinterpret_cast<const float4 *>(zc + s * 16 + hf * 8 + 4);
+      zdot += bf_lo(w.x) * z0.x + bf_hi(w.x) * z0.y + bf_lo(w.y) * z0.z + bf_hi(w.y) * z0.w +
+              bf_lo(w.z) * z1.x + bf_hi(w.z) * z1.y + bf_lo(w.w) * z1.z + bf_hi(w.w) * z1.w;
+    }
+    const float den = zdot + __shfl_xor(zdot, 32);
+    inv_l = den > 0.0f ? 1.0f / den : 0.0f;
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+  }
+  const char *hv = (n & 1) ? v1s : v0s;   // H_C^T rows 0..63
+  const char *hk = (n & 1) ? k1s : k0s;   // H_C^T rows 64..
+  uint16_t *orow = og + (size_t)qrow * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    floatx16 lacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lacc[i] = 0.0f;
+    if (lin_on) {
+      const int d = t * 32 + l32;
+      const char *hrow = d < 64 ? hv + d * VROWB : hk + (d - 64) * VROWB;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(hrow + (((2 * s + hf) ^ (d & (HG - 1))) * 16));
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[s], lacc, 0, 0, 0);
+      }
+    }
+    if (q_ok) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = t * 32 + g * 8 + hf * 4;
-        float o0 = oacc[t][g * 4 + 0] * inv, o1 = oacc[t][g * 4 + 1] * inv;
-        float o2 = oacc[t][g * 4 + 2] * inv, o3 = oacc[t][g * 4 + 3] * inv;
-        if constexpr (LIN) {
-          // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel)
-          const int h = bh % a.H;
-          const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)h * D + d);
-          const float4 lv = *reinterpret_cast<const float4 *>(a.ol + head + (size_t)qi * D + d);
-          o0 = al.x * o0 + (1.f - al.x) * lv.x;
-          o1 = al.y * o1 + (1.f - al.y) * lv.y;
-          o2 = al.z * o2 + (1.f - al.z) * lv.z;
-          o3 = al.w * o3 + (1.f - al.w) * lv.w;
-        }
+        // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel)
+        const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)(bh % a.H) * D + d);
+        const float o0 = al.x * (oacc[t][g * 4 + 0] * inv) + (1.f - al.x) * (lacc[g * 4 + 0] * inv_l);
+        const float o1 = al.y * (oacc[t][g * 4 + 1] * inv) + (1.f - al.y) * (lacc[g * 4 + 1] * inv_l);
+        const float o2 = al.z * (oacc[t][g * 4 + 2] * inv) + (1.f - al.z) * (lacc[g * 4 + 2] * inv_l);
+        const float o3 = al.w * (oacc[t][g * 4 + 3] * inv) + (1.f - al.w) * (lacc[g * 4 + 3] * inv_l);
         *reinterpret_cast<uint2 *>(orow + d) = pack4(o0, o1, o2, o3);
       }
-    if (a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+    }
   }
+  if (q_ok && a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
 template <int D, bool LIN, bool GATHER>

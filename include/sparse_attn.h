@@ -154,7 +154,9 @@ sa_status sparse_attn_plan_ordered(const void *q, const void *k, sa_dtype dtype,
                                    sa_plan *out, hipStream_t stream);
 
 /* Workspace bytes sparse_attn_fwd needs with this plan: 0 without the linear branch
- * (with_linear = 0); 0 as well when plan is NULL or describes an unsupported shape. */
+ * (with_linear = 0); 0 as well when plan is NULL or describes an unsupported shape. With
+ * it: per head the totals H (fp32 D x D) and z, their per-chunk partials and phi(K) in
+ * bf16, and per query block its masked-out sums H_C^T (bf16 D x D) and z_C (fp32). */
 size_t sparse_attn_fwd_workspace_bytes(const sa_plan *plan, int with_linear);
 
 /* Block-sparse attention over the plan's kept tiles (SpargeAttention2 page, section 2(3)).

@@ -59,8 +59,10 @@ def test_workspace_sizes(lib):
     st.B, st.H, st.N, st.D, st.block_q, st.block_kv = 1, 12, 32760, 128, 128, 64
     assert lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 0) == 0
     lin = lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 1)
-    # at least H and z per head, and Ol in fp32
-    assert lin >= 12 * (128 * 128 + 128) * 4 + 12 * 32760 * 128 * 4
+    # at least H and z per head, phi(K) over whole KV blocks, and per query block the
+    # masked-out sums H_C^T (bf16) and z_C (fp32)
+    R, n_pad = 12 * 256, 512 * 64
+    assert lin >= 12 * (128 * 128 + 128) * 4 + 12 * n_pad * 128 * 2 + R * (128 * 128 * 2 + 128 * 4)
     assert lib.sparse_attn_fwd_workspace_bytes(None, 1) == 0
     st.D = 96
     assert lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 1) == 0
