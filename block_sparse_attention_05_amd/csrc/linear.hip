@@ -316,6 +316,23 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   const uint16_t *vg = reinterpret_cast<const uint16_t *>(a.v) + head;
   const uint16_t *pk = lb.phik + (size_t)bh * lb.n_pad * D;
 
+  // The accumulators start from the head's total H when the kept tiles are subtracted
+  // (their phi(K) operands then enter negated, an exact sign flip), so H_C = H - H_S forms
+  // in fp32 inside the MFMA chain. H is read before the row's CSR range is known, so its
+  // loads overlap that round trip; rows that sum the complement drop it.
+  const float *hg = lb.h + (size_t)bh * D * D;
+  floatx16 hacc[WC][WD];
+#pragma unroll
+  for (int x = 0; x < WC; ++x)
+#pragma unroll
+    for (int y = 0; y < WD; ++y)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = (cp * WC + x) * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
+        const int d = (dp * WD + y) * 32 + l32;
+        hacc[x][y][i] = hg[(size_t)c * D + d];
+      }
+
   const int beg = a.row_ptr[row], end = a.row_ptr[row + 1];
   const int kept = end - beg;
   if (kept == nKV) return;  // empty complement: the forward takes Ol = 0 without reading
@@ -404,13 +421,13 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
 #pragma unroll
   for (int y = 0; y < WD; ++y) voff[y] = rbase + (((dp * WD + y) ^ ((u >> 2) & (VSEG - 1))) * 64);
 
-  floatx16 hacc[WC][WD];
 #pragma unroll
   for (int x = 0; x < WC; ++x)
 #pragma unroll
     for (int y = 0; y < WD; ++y)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) hacc[x][y][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) hacc[x][y][i] = subtract ? hacc[x][y][i] : 0.0f;
+  const uint32_t neg = subtract ? 0x80008000u : 0u;
   float zacc[WC];
 #pragma unroll
   for (int x = 0; x < WC; ++x) zacc[x] = 0.0f;
@@ -451,10 +468,17 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
           }
       }
 #pragma unroll
-      for (int x = 0; x < WC; ++x)
+      for (int x = 0; x < WC; ++x) {
+        uint4 w = __builtin_bit_cast(uint4, av[x]);
+        w.x ^= neg;
+        w.y ^= neg;
+        w.z ^= neg;
+        w.w ^= neg;
+        const bf16x8_t an = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
         for (int y = 0; y < WD; ++y)
-          hacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], hacc[x][y], 0, 0, 0);
+          hacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(an, bv[y], hacc[x][y], 0, 0, 0);
+      }
     }
   };
 
@@ -482,19 +506,7 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
     const float zz = zacc[x] + __shfl_xor(zacc[x], 32);
     if (hf == 0) zs[dp * D + (cp * WC + x) * 32 + l32] = zz;
   }
-  // H_C = H - H_S (subtract) or H_S, in fp32, then rounded once to bf16
-  const float *hg = lb.h + (size_t)bh * D * D;
-  float hc[WC][WD][16];
-#pragma unroll
-  for (int x = 0; x < WC; ++x)
-#pragma unroll
-    for (int y = 0; y < WD; ++y)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = (cp * WC + x) * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
-        const int d = (dp * WD + y) * 32 + l32;
-        hc[x][y][i] = subtract ? hg[(size_t)c * D + d] - hacc[x][y][i] : hacc[x][y][i];
-      }
+  // H_C (H - H_S or H_S) in fp32, rounded once to bf16 below
   __syncthreads();  // every wave is done with the stage buffers
   // staged H_C^T: row d in the stage buffers (2 * SK rows each), 16-byte granule c/8 at
   // physical granule (c/8) ^ (d mod HG)
@@ -510,7 +522,7 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int gr = (cp * WC + x) * 4 + q4;
         *reinterpret_cast<uint2 *>(hrow + ((gr ^ (d & (HG - 1))) * 16) + hf * 8) =
-            pack4(hc[x][y][q4 * 4 + 0], hc[x][y][q4 * 4 + 1], hc[x][y][q4 * 4 + 2], hc[x][y][q4 * 4 + 3]);
+            pack4(hacc[x][y][q4 * 4 + 0], hacc[x][y][q4 * 4 + 1], hacc[x][y][q4 * 4 + 2], hacc[x][y][q4 * 4 + 3]);
       }
     }
   __syncthreads();
