@@ -3,8 +3,10 @@
 One step = sparse_attn_plan (pool, scores, hybrid top-k/top-p select, CSR) followed by
 sparse_attn_fwd over the kept tiles, on seeded synthetic video-token Q, K, V already
 resident in HBM. By default the step goes through sparse_attn_pipelined, which runs the
-two over chunks of heads on two streams (--chunks; by default 4 chunks on steps of at least 8192 query-block rows); the plain plan-then-forward
-sequence is timed as well (ms_step_sequential, ms_plan, ms_fwd). Prints one JSON line:
+two over chunks of heads on two streams (--chunks; by default 4 chunks on steps of at
+least 8192 query-block rows, and one chunk below that with the linear branch, whose
+prepass then runs beside the plan); the plain plan-then-forward sequence is timed as well
+(ms_step_sequential, ms_plan, ms_fwd). Prints one JSON line:
 
   value        effective TFLOP/s over the exact kept query-key pairs (4*D flops per
                pair) per step, plan included
@@ -184,6 +186,15 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (int8: 5.0 POP/s, the sam
 PIPE_MIN_ROWS = 8192
 
 
+def default_chunks(w) -> int:
+    """Chunks of heads for the pipelined step: 4 from PIPE_MIN_ROWS rows up; below that one
+    chunk with the linear branch (its prepass, which needs no mask, runs beside the plan on
+    the second stream), else none (the plain plan-then-forward sequence)."""
+    if w.B * w.H * w.n_qblk >= PIPE_MIN_ROWS:
+        return 4
+    return 1 if w.linear else 0
+
+
 def time_fp8(sa, torch, w, dq, dk, dv, p, flops, t_fwd_bf16, args, stream):
     """Times the low-bit forward over the plan p for both q/k formats (E4M3, int8; v is
     E4M3 in both): the quantiser and the attention kernel, each with HIP events on the
@@ -302,18 +313,25 @@ def other_config(sa, torch, w: W.Workload, steps: int, warmup: int, dense: bool 
     res = {"B": w.B, "H": w.H, "N": w.N, "D": w.D, "dtype": w.dtype, "block_q": w.block_q,
            "block_kv": w.block_kv, "topk": w.topk, "top_p": w.top_p, "linear_branch": bool(w.linear),
            "ms_plan": round(t_plan, 4), "ms_fwd": round(t_fwd, 4), "ms_step_sequential": round(t_step, 4)}
-    if w.rows >= PIPE_MIN_ROWS and not w.linear:
+    chunks = default_chunks(w)
+    if chunks:
+        pws = torch.empty(sa.pipelined_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv, chunks,
+                                                       linear=bool(w.linear)), dtype=torch.uint8, device="cuda")
         for _ in range(max(1, warmup)):
-            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=4, out=o)
+            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=chunks, out=o,
+                         workspace=pws, alpha=dalpha)
         e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         for a_, b_ in zip(e0, e1):
             a_.record(stream)
-            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=4, out=o)
+            sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=chunks, out=o,
+                         workspace=pws, alpha=dalpha)
             b_.record(stream)
         torch.cuda.synchronize()
         t_step = float(np.mean([a_.elapsed_time(b_) for a_, b_ in zip(e0, e1)]))
         res["ms_step_pipelined"] = round(t_step, 4)
+        res["pipeline_chunks"] = chunks
+        del pws
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     nnz = int(rp[-1])
     res.update({
@@ -474,16 +492,17 @@ def main():
     t_seq = t_step
     ms_seq = ms_step
     if args.chunks is None:
-        args.chunks = 4 if w.B * w.H * w.n_qblk >= PIPE_MIN_ROWS else 0
-    pipelined = args.chunks > 0 and q_table is None and not w.linear
+        args.chunks = default_chunks(w)
+    pipelined = args.chunks > 0 and q_table is None
     if pipelined:
         # the step through the pipelined call: plan + forward over head chunks, two streams
-        pws = torch.empty(sa.pipelined_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv, args.chunks),
+        pws = torch.empty(sa.pipelined_workspace_bytes(w.B, w.H, w.N, w.D, w.block_q, w.block_kv, args.chunks,
+                                                       linear=bool(w.linear)),
                           dtype=torch.uint8, device="cuda")
 
         def pstep():
             sa.attention(dq, dk, dv, w.block_q, w.block_kv, w.topk, w.top_p, chunks=args.chunks, out=o,
-                         workspace=pws)
+                         workspace=pws, alpha=dalpha)
         for _ in range(args.warmup):
             pstep()
         p0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]

@@ -90,9 +90,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, pplan, vp, vp, vp,
                                     vp, sz, vp]
     lib.sparse_attn_bwd.restype = i32
-    lib.sparse_attn_pipelined_workspace_bytes.argtypes = [i32] * 7
+    lib.sparse_attn_pipelined_workspace_bytes.argtypes = [i32] * 8
     lib.sparse_attn_pipelined_workspace_bytes.restype = sz
-    lib.sparse_attn_pipelined.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [dbl, dbl, i32, vp, vp, vp, sz, vp, vp]
+    lib.sparse_attn_pipelined.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [dbl, dbl, i32, vp, vp, vp, vp, sz, vp, vp]
     lib.sparse_attn_pipelined.restype = i32
     lib.sparse_attn_pipelined_noalloc.argtypes = [vp, vp, vp, i32] + [i32] * 6 + [dbl, dbl, vp, vp, vp]
     lib.sparse_attn_pipelined_noalloc.restype = i32
@@ -494,20 +494,26 @@ def _aux_stream(device):
     return _AUX[key]
 
 
-def pipelined_workspace_bytes(B, H, N, D, block_q=128, block_kv=64, chunks=4) -> int:
-    return int(load_library().sparse_attn_pipelined_workspace_bytes(B, H, N, D, block_q, block_kv, chunks))
+def pipelined_workspace_bytes(B, H, N, D, block_q=128, block_kv=64, chunks=4, linear=False) -> int:
+    return int(load_library().sparse_attn_pipelined_workspace_bytes(B, H, N, D, block_q, block_kv, chunks,
+                                                                     1 if linear else 0))
 
 
 def attention(q, k, v, block_q: int = 128, block_kv: int = 64, topk: float = 0.05, top_p: float = 0.9,
               chunks: int = 4, return_lse: bool = False, out=None, lse=None, workspace=None, stream=None,
-              aux_stream=None):
+              aux_stream=None, alpha=None):
     """Plan and forward for all heads in one call, pipelined over chunks of heads on two
-    streams (see sparse_attn_pipelined). Returns o (and lse with return_lse)."""
+    streams (see sparse_attn_pipelined); alpha [H, D] float32 adds the linear branch as in
+    fwd. Returns o (and lse with return_lse)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    need = lib.sparse_attn_pipelined_workspace_bytes(B, H, N, D, block_q, block_kv, chunks)
+    if alpha is not None and not (alpha.is_cuda and alpha.dtype == torch.float32 and alpha.is_contiguous()
+                                  and tuple(alpha.shape) == (H, D)):
+        raise ValueError("alpha must be a contiguous float32 [H, D] GPU tensor")
+    need = lib.sparse_attn_pipelined_workspace_bytes(B, H, N, D, block_q, block_kv, chunks,
+                                                     0 if alpha is None else 1)
     if need == 0:
         raise SparseAttnError(SA_ERR_UNSUPPORTED, "pipelined shape")
     ws = workspace if workspace is not None else _new_ws(need, q.device)
@@ -518,7 +524,8 @@ def attention(q, k, v, block_q: int = 128, block_kv: int = 64, topk: float = 0.0
     s = stream if stream is not None else torch.cuda.current_stream()
     aux = aux_stream if aux_stream is not None else _aux_stream(q.device)
     _check(lib.sparse_attn_pipelined(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, N, D,
-                                     block_q, block_kv, float(topk), float(top_p), int(chunks), o.data_ptr(),
+                                     block_q, block_kv, float(topk), float(top_p), int(chunks),
+                                     None if alpha is None else alpha.data_ptr(), o.data_ptr(),
                                      lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(),
                                      s.cuda_stream, aux.cuda_stream), "sparse_attn_pipelined")
     return (o, lse) if return_lse else o

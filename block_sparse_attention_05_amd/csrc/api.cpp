@@ -282,9 +282,17 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_plan *plan, int with_linear) {
   return fwd_layout(s, with_linear).total;
 }
 
-sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype dtype, int B,
-                          int H, int N, int D, const sa_plan *plan, const float *alpha, void *o,
-                          float *lse, void *workspace, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// The forward in two parts that the pipelined call runs apart: the linear branch's
+// prepass (k and v only, no plan needed on the device) and the rest (the linear apply
+// step, then the attention). sparse_attn_fwd runs both. alpha_h0 / alpha_H: head h of
+// this call takes alpha row (alpha_h0 + h) % alpha_H (0 and H for a whole tensor).
+enum { kPartPrepass = 1, kPartAttend = 2 };
+sa_status fwd_impl(const void *q, const void *k, const void *v, sa_dtype dtype, int B, int H, int N, int D,
+                   const sa_plan *plan, const float *alpha, int alpha_h0, int alpha_H, void *o, float *lse,
+                   void *workspace, size_t ws_bytes, hipStream_t stream, int parts) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || plan == nullptr)
     return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
@@ -325,6 +333,8 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   a.scale_log2_f64 = 1.4426950408889634 / sqrt((double)D);
   a.alpha = nullptr;
+  a.alpha_h0 = 0;
+  a.alpha_H = 1;
   a.hct = nullptr;
   a.zc = nullptr;
   if (alpha != nullptr) {
@@ -338,14 +348,28 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
     lb.z = reinterpret_cast<float *>(ws + L.lin_z);
     lb.hct = reinterpret_cast<uint16_t *>(ws + L.hct);
     lb.zc = reinterpret_cast<float *>(ws + L.zc);
-    hipError_t e = launch_linear_prepass(k, v, dtype, B * H, N, D, lb, stream);
-    if (e == hipSuccess) e = launch_linear_apply(a, lb, stream);
+    hipError_t e = hipSuccess;
+    if (parts & kPartPrepass) e = launch_linear_prepass(k, v, dtype, B * H, N, D, lb, stream);
+    if (e == hipSuccess && (parts & kPartAttend)) e = launch_linear_apply(a, lb, stream);
     if (e != hipSuccess) return SA_ERR_HIP;
     a.alpha = alpha;
+    a.alpha_h0 = alpha_h0;
+    a.alpha_H = alpha_H;
     a.hct = lb.hct;
     a.zc = lb.zc;
   }
+  if (!(parts & kPartAttend)) return SA_OK;
   return hip_status(launch_fwd(a, dtype, stream));
+}
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype dtype, int B,
+                          int H, int N, int D, const sa_plan *plan, const float *alpha, void *o,
+                          float *lse, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return fwd_impl(q, k, v, dtype, B, H, N, D, plan, alpha, 0, H, o, lse, workspace, ws_bytes, stream,
+                  kPartPrepass | kPartAttend);
 }
 
 namespace {
@@ -378,12 +402,14 @@ hipEvent_t *pipeline_events(int n) {
 }
 
 // The pipelined call splits the B*H heads into chunks of `per` heads, each planned in its
-// own plan workspace.
+// own plan workspace; with the linear branch one forward workspace for a chunk follows
+// (the chunks' forwards run in order on one stream and reuse it).
 struct PipeLayout {
   int C, per;
-  size_t plan_bytes, total;
+  size_t plan_bytes, lin_off, total;
 };
-sa_status pipe_layout(int B, int H, int N, int D, int bq, int bk, int n_chunks, PipeLayout *L) {
+sa_status pipe_layout(int B, int H, int N, int D, int bq, int bk, int n_chunks, int with_linear,
+                      PipeLayout *L) {
   Shape s;
   sa_status st = check_shape(B, H, N, D, bq, bk, &s);
   if (st != SA_OK) return st;
@@ -395,27 +421,29 @@ sa_status pipe_layout(int B, int H, int N, int D, int bq, int bk, int n_chunks, 
   st = check_shape(1, L->per, N, D, bq, bk, &s1);
   if (st != SA_OK) return st;
   L->plan_bytes = plan_layout(s1).total;
-  L->total = L->plan_bytes * L->C;
+  L->lin_off = align_up(L->plan_bytes * L->C);
+  L->total = L->lin_off + (with_linear ? fwd_layout(s1, 1).total : 0);
   return SA_OK;
 }
 }  // namespace
 
 size_t sparse_attn_pipelined_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv,
-                                             int n_chunks) {
+                                             int n_chunks, int with_linear) {
   PipeLayout L;
-  if (pipe_layout(B, H, N, D, block_q, block_kv, n_chunks, &L) != SA_OK) return 0;
+  if (pipe_layout(B, H, N, D, block_q, block_kv, n_chunks, with_linear, &L) != SA_OK) return 0;
   return L.total;
 }
 
 sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_dtype dtype, int B, int H,
                                 int N, int D, int block_q, int block_kv, double topk_frac, double top_p,
-                                int n_chunks, void *o, float *lse, void *workspace, size_t ws_bytes,
-                                hipStream_t stream, hipStream_t aux_stream) {
+                                int n_chunks, const float *alpha, void *o, float *lse, void *workspace,
+                                size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
   if (!(topk_frac >= 0.0 && topk_frac <= 1.0) || !(top_p >= 0.0 && top_p <= 1.0)) return SA_ERR_INVALID_ARG;
+  if (alpha != nullptr && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;  // linear branch: bf16
   PipeLayout L;
-  sa_status st = pipe_layout(B, H, N, D, block_q, block_kv, n_chunks, &L);
+  sa_status st = pipe_layout(B, H, N, D, block_q, block_kv, n_chunks, alpha != nullptr, &L);
   if (st != SA_OK) return st;
   st = check_ws(workspace, ws_bytes, L.total);
   if (st != SA_OK) return st;
@@ -444,16 +472,29 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
                    two ? aux_stream : stream);
     if (st == SA_OK && two && hipEventRecord(ev[c], aux_stream) != hipSuccess) st = SA_ERR_HIP;
   }
+  // With the linear branch, chunk c's prepass (k and v only) goes on `stream` before the
+  // wait for its plan, so the first one runs beside the first plan.
+  char *lin_ws = alpha ? static_cast<char *>(workspace) + L.lin_off : nullptr;
+  const size_t lin_bytes = L.total - L.lin_off;
   for (int c = 0; c < L.C && st == SA_OK; ++c) {
     const int hc = BH - c * L.per < L.per ? BH - c * L.per : L.per;
+    const char *qc = chunk(c, static_cast<const char *>(q));
+    const char *kc = chunk(c, static_cast<const char *>(k));
+    const char *vc = chunk(c, static_cast<const char *>(v));
+    char *oc = const_cast<char *>(chunk(c, static_cast<const char *>(o)));
+    float *lc = lse ? lse + (size_t)c * L.per * N : nullptr;
+    const int h0 = (c * L.per) % H;
+    if (alpha) {
+      st = fwd_impl(qc, kc, vc, dtype, 1, hc, N, D, &plans[c], alpha, h0, H, oc, lc, lin_ws, lin_bytes, stream,
+                    kPartPrepass);
+      if (st != SA_OK) break;
+    }
     if (two && hipStreamWaitEvent(stream, ev[c], 0) != hipSuccess) {
       st = SA_ERR_HIP;
       break;
     }
-    float *lc = lse ? lse + (size_t)c * L.per * N : nullptr;
-    st = sparse_attn_fwd(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)),
-                         chunk(c, static_cast<const char *>(v)), dtype, 1, hc, N, D, &plans[c], nullptr,
-                         const_cast<char *>(chunk(c, static_cast<const char *>(o))), lc, nullptr, 0, stream);
+    st = fwd_impl(qc, kc, vc, dtype, 1, hc, N, D, &plans[c], alpha, h0, H, oc, lc, lin_ws, lin_bytes, stream,
+                  kPartAttend);
   }
   return st;
 }

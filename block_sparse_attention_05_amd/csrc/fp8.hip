@@ -475,12 +475,22 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
           if (key >= valid) sacc[kt][i] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    // the tile max in four independent chains of eight, then the other lane half's max by
+    // v_permlane32_swap (each lane gets the pair {own, partner}; no LDS round trip)
+    float mc[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int c = 0; c < 4; ++c) {
+      const int kt = c >> 1, i0 = (c & 1) * 8;
+      float m = sacc[kt][i0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = 1; i < 8; ++i) m = fmaxf(m, sacc[kt][i0 + i]);
+      mc[c] = m;
+    }
+    float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mt = mx * mul;
     const bool need = mt > m_run + lazy;
     if (__ballot(need)) {

@@ -44,7 +44,8 @@ struct FwdArgs {
   float scale_log2;        // log2(e) / sqrt(D)
   double scale_log2_f64;   // the same in fp64
   // linear branch (null alpha: off)
-  const float *alpha;      // [H, D]
+  const float *alpha;      // [alpha_H, D]: head h of this call uses row (alpha_h0 + h) % alpha_H
+  int alpha_h0, alpha_H;
   const uint16_t *hct;     // [R, D, D] bf16 per plan row: H_C^T, row d = value channel
   const float *zc;         // [R, D] fp32 per plan row: z_C
 };

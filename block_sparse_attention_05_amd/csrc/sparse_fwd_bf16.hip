@@ -515,7 +515,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d = t * 32 + g * 8 + hf * 4;
         // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel)
-        const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)(bh % a.H) * D + d);
+        const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)((a.alpha_h0 + bh) % a.alpha_H) * D + d);
         const float o0 = al.x * (oacc[t][g * 4 + 0] * inv) + (1.f - al.x) * (lacc[g * 4 + 0] * inv_l);
         const float o1 = al.y * (oacc[t][g * 4 + 1] * inv) + (1.f - al.y) * (lacc[g * 4 + 1] * inv_l);
         const float o2 = al.z * (oacc[t][g * 4 + 2] * inv) + (1.f - al.z) * (lacc[g * 4 + 2] * inv_l);

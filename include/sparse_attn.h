@@ -177,17 +177,22 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
                           const float *alpha, void *o, float *lse,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes sparse_attn_pipelined needs: one plan workspace per chunk of heads. */
+/* Workspace bytes sparse_attn_pipelined needs: one plan workspace per chunk of heads and,
+ * with the linear branch (with_linear != 0), one forward workspace for a chunk. */
 size_t sparse_attn_pipelined_workspace_bytes(int B, int H, int N, int D, int block_q, int block_kv,
-                                             int n_chunks);
+                                             int n_chunks, int with_linear);
 
-/* The two hot-path calls, sparse_attn_plan then sparse_attn_fwd (without the linear
- * branch), for all B*H heads, pipelined over chunks of heads: the B*H (batch, head)
- * pairs are split into ceil(B*H / ceil(B*H / n_chunks)) chunks of consecutive pairs.
+/* The two hot-path calls, sparse_attn_plan then sparse_attn_fwd, for all B*H heads,
+ * pipelined over chunks of heads: the B*H (batch, head) pairs are split into
+ * ceil(B*H / ceil(B*H / n_chunks)) chunks of consecutive pairs.
  * The chunks' plans run back to back on aux_stream and their forwards on `stream`, each
  * forward after its chunk's plan, so every plan but the first (a chain of small,
- * latency-bound kernels) runs under the forwards of earlier chunks. A head's mask depends
- * on that head alone, so o and lse equal those of the two-call path bit for bit.
+ * latency-bound kernels) runs under the forwards of earlier chunks. alpha: as for
+ * sparse_attn_fwd (device float [H, D], or NULL for no linear branch; bf16 only). With
+ * it, each chunk's linear prepass (which reads k and v, not the mask) is enqueued on
+ * `stream` before the wait for that chunk's plan, so even with n_chunks = 1 it runs beside
+ * the plan. A head's mask depends on that head alone, so o and lse equal those of the
+ * two-call path bit for bit.
  * Ordering: the plans on aux_stream start after the work enqueued on `stream` before this
  * call; every forward is on `stream`, so later work there follows them. aux_stream may
  * equal stream (plans and forwards then run in order). The plans live in the workspace and
@@ -200,13 +205,13 @@ size_t sparse_attn_pipelined_workspace_bytes(int B, int H, int N, int D, int blo
  * thread; it creates and destroys nothing per call. */
 sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_dtype dtype,
                                 int B, int H, int N, int D, int block_q, int block_kv,
-                                double topk_frac, double top_p, int n_chunks, void *o,
-                                float *lse, void *workspace, size_t ws_bytes,
-                                hipStream_t stream, hipStream_t aux_stream);
+                                double topk_frac, double top_p, int n_chunks,
+                                const float *alpha, void *o, float *lse, void *workspace,
+                                size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
- * serving loops, harnesses that forbid hipMalloc): sparse_attn_pipelined with one stream
- * and no workspace argument. The plan workspaces live in a static device array of the
+ * serving loops, harnesses that forbid hipMalloc): sparse_attn_pipelined with one stream,
+ * no workspace argument and no linear branch. The plan workspaces live in a static device array of the
  * library, 128 MiB per device (every device the library runs on holds it until the
  * process ends). Heads are taken in chunks of equal size, as many heads per chunk as fit
  * in that array; each chunk is planned and then attended on `stream` before the next

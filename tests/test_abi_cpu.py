@@ -406,20 +406,33 @@ def test_pipelined_noalloc_validation(lib):
 def test_pipelined_validation(lib):
     f = lib.sparse_attn_pipelined_workspace_bytes
     one = lib.sparse_attn_plan_workspace_bytes(1, 5, 75600, 128, 128, 64)
-    assert f(1, 40, 75600, 128, 128, 64, 8) == 8 * one          # eight chunks of five heads
-    assert f(2, 3, 1000, 64, 64, 64, 4) == 3 * lib.sparse_attn_plan_workspace_bytes(1, 2, 1000, 64, 64, 64)
-    assert f(1, 4, 1000, 64, 64, 64, 100) == 4 * lib.sparse_attn_plan_workspace_bytes(1, 1, 1000, 64, 64, 64)
-    assert f(1, 4, 1000, 64, 64, 64, 0) == 0
-    assert f(1, 4, 1000, 80, 64, 64, 2) == 0
-    need = f(1, 2, 1024, 64, 64, 64, 2)
+    assert f(1, 40, 75600, 128, 128, 64, 8, 0) == 8 * one          # eight chunks of five heads
+    assert f(2, 3, 1000, 64, 64, 64, 4, 0) == 3 * lib.sparse_attn_plan_workspace_bytes(1, 2, 1000, 64, 64, 64)
+    assert f(1, 4, 1000, 64, 64, 64, 100, 0) == 4 * lib.sparse_attn_plan_workspace_bytes(1, 1, 1000, 64, 64, 64)
+    assert f(1, 4, 1000, 64, 64, 64, 0, 0) == 0
+    assert f(1, 4, 1000, 80, 64, 64, 2, 0) == 0
+    # with the linear branch: the plan workspaces, then one chunk's forward workspace
+    st = B.SaPlan()
+    st.B, st.H, st.N, st.D, st.block_q, st.block_kv = 1, 3, 32760, 128, 128, 64
+    lin = lib.sparse_attn_fwd_workspace_bytes(ctypes.byref(st), 1)
+    plans = f(1, 12, 32760, 128, 128, 64, 4, 0)
+    assert plans == 4 * lib.sparse_attn_plan_workspace_bytes(1, 3, 32760, 128, 128, 64)
+    assert f(1, 12, 32760, 128, 128, 64, 4, 1) == -(-plans // 256) * 256 + lin
+    need = f(1, 2, 1024, 64, 64, 64, 2, 0)
+    need_lin = f(1, 2, 1024, 64, 64, 64, 2, 1)
+    assert need_lin > need
     g = lib.sparse_attn_pipelined
 
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, shape=(1, 2, 1024, 64), bq=64, bk=64, k_=0.1, p=0.9, C=2,
-                 o=FAKE, lse=None, ws=FAKE, wsb=need)
+                 alpha=None, o=FAKE, lse=None, ws=FAKE, wsb=need)
         a.update(kw)
         return g(a["q"], a["k"], a["v"], a["dt"], *a["shape"], a["bq"], a["bk"], a["k_"], a["p"], a["C"],
-                 a["o"], a["lse"], a["ws"], a["wsb"], None, None)
+                 a["alpha"], a["o"], a["lse"], a["ws"], a["wsb"], None, None)
+
+    # the linear branch needs its forward workspace too, and bf16
+    assert call(alpha=FAKE, wsb=need) == B.SA_ERR_WORKSPACE
+    assert call(alpha=FAKE, dt=1, wsb=need_lin) == B.SA_ERR_UNSUPPORTED
 
     for name in ("q", "k", "v", "o"):
         assert call(**{name: None}) == B.SA_ERR_INVALID_ARG, name
