@@ -140,10 +140,12 @@ size_t sparse_attn_plan_workspace_bytes(int B, int H, int N, int D, int block_q,
 }
 
 namespace {
+// mask_done: NULL, or an event recorded on `stream` once the CSR is written (before the
+// work order), for work that needs the mask but not the order.
 sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, int N, int D,
                     int block_q, int block_kv, double topk_frac, double top_p,
                     const int32_t *q_order, const int32_t *kv_order, void *workspace, size_t ws_bytes,
-                    sa_plan *out, hipStream_t stream) {
+                    sa_plan *out, hipStream_t stream, hipEvent_t mask_done = nullptr) {
   if (q == nullptr || k == nullptr || out == nullptr) return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
   if (!(topk_frac >= 0.0 && topk_frac <= 1.0)) return SA_ERR_INVALID_ARG;
@@ -186,6 +188,7 @@ sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, 
                       stream);
   if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, p.nnz, stream);
   if (e == hipSuccess) e = launch_fill(bitmap, nwords, p.row_ptr, (int)s.R, p.col_idx, stream);
+  if (e == hipSuccess && mask_done != nullptr) e = hipEventRecord(mask_done, stream);
   if (e == hipSuccess)
     e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
@@ -285,11 +288,12 @@ size_t sparse_attn_fwd_workspace_bytes(const sa_plan *plan, int with_linear) {
 }  // extern "C"
 
 namespace {
-// The forward in two parts that the pipelined call runs apart: the linear branch's
-// prepass (k and v only, no plan needed on the device) and the rest (the linear apply
-// step, then the attention). sparse_attn_fwd runs both. alpha_h0 / alpha_H: head h of
-// this call takes alpha row (alpha_h0 + h) % alpha_H (0 and H for a whole tensor).
-enum { kPartPrepass = 1, kPartAttend = 2 };
+// The forward in three parts that the pipelined call runs apart: the linear branch's
+// prepass (k and v only, no plan needed on the device), its apply step (needs the mask's
+// CSR, not the plan's work order) and the attention. sparse_attn_fwd runs all three.
+// alpha_h0 / alpha_H: head h of this call takes alpha row (alpha_h0 + h) % alpha_H (0 and
+// H for a whole tensor).
+enum { kPartPrepass = 1, kPartApply = 2, kPartAttention = 4 };
 sa_status fwd_impl(const void *q, const void *k, const void *v, sa_dtype dtype, int B, int H, int N, int D,
                    const sa_plan *plan, const float *alpha, int alpha_h0, int alpha_H, void *o, float *lse,
                    void *workspace, size_t ws_bytes, hipStream_t stream, int parts) {
@@ -350,7 +354,7 @@ sa_status fwd_impl(const void *q, const void *k, const void *v, sa_dtype dtype, 
     lb.zc = reinterpret_cast<float *>(ws + L.zc);
     hipError_t e = hipSuccess;
     if (parts & kPartPrepass) e = launch_linear_prepass(k, v, dtype, B * H, N, D, lb, stream);
-    if (e == hipSuccess && (parts & kPartAttend)) e = launch_linear_apply(a, lb, stream);
+    if (e == hipSuccess && (parts & kPartApply)) e = launch_linear_apply(a, lb, stream);
     if (e != hipSuccess) return SA_ERR_HIP;
     a.alpha = alpha;
     a.alpha_h0 = alpha_h0;
@@ -358,7 +362,7 @@ sa_status fwd_impl(const void *q, const void *k, const void *v, sa_dtype dtype, 
     a.hct = lb.hct;
     a.zc = lb.zc;
   }
-  if (!(parts & kPartAttend)) return SA_OK;
+  if (!(parts & kPartAttention)) return SA_OK;
   return hip_status(launch_fwd(a, dtype, stream));
 }
 }  // namespace
@@ -369,7 +373,7 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, sa_dtype 
                           int H, int N, int D, const sa_plan *plan, const float *alpha, void *o,
                           float *lse, void *workspace, size_t ws_bytes, hipStream_t stream) {
   return fwd_impl(q, k, v, dtype, B, H, N, D, plan, alpha, 0, H, o, lse, workspace, ws_bytes, stream,
-                  kPartPrepass | kPartAttend);
+                  kPartPrepass | kPartApply | kPartAttention);
 }
 
 namespace {
@@ -455,9 +459,11 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
   const bool two = aux_stream != stream;
   // Plans go on aux_stream back to back; forwards on `stream`, each after its chunk's plan.
   // Only the first plan is exposed; the others run under the forwards before them.
+  // ev[c]: chunk c's plan done; ev[L.C]: the caller's earlier work; ev[L.C + 1 + c]: chunk
+  // c's CSR written (the linear apply step waits only for that)
   hipEvent_t *ev = nullptr;
   if (two) {
-    ev = pipeline_events(L.C + 1);
+    ev = pipeline_events(alpha ? 2 * L.C + 1 : L.C + 1);
     if (ev == nullptr) return SA_ERR_HIP;
     // the plans start after the caller's earlier work on `stream` (inputs written there)
     if (hipEventRecord(ev[L.C], stream) != hipSuccess || hipStreamWaitEvent(aux_stream, ev[L.C], 0) != hipSuccess)
@@ -469,7 +475,7 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
     char *ws = static_cast<char *>(workspace) + c * L.plan_bytes;
     st = plan_impl(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)), dtype, 1, hc,
                    N, D, block_q, block_kv, topk_frac, top_p, nullptr, nullptr, ws, L.plan_bytes, &plans[c],
-                   two ? aux_stream : stream);
+                   two ? aux_stream : stream, two && alpha ? ev[L.C + 1 + c] : nullptr);
     if (st == SA_OK && two && hipEventRecord(ev[c], aux_stream) != hipSuccess) st = SA_ERR_HIP;
   }
   // With the linear branch, chunk c's prepass (k and v only) goes on `stream` before the
@@ -487,6 +493,10 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
     if (alpha) {
       st = fwd_impl(qc, kc, vc, dtype, 1, hc, N, D, &plans[c], alpha, h0, H, oc, lc, lin_ws, lin_bytes, stream,
                     kPartPrepass);
+      if (st == SA_OK && two && hipStreamWaitEvent(stream, ev[L.C + 1 + c], 0) != hipSuccess) st = SA_ERR_HIP;
+      if (st == SA_OK)
+        st = fwd_impl(qc, kc, vc, dtype, 1, hc, N, D, &plans[c], alpha, h0, H, oc, lc, lin_ws, lin_bytes,
+                      stream, kPartApply);
       if (st != SA_OK) break;
     }
     if (two && hipStreamWaitEvent(stream, ev[c], 0) != hipSuccess) {
@@ -494,7 +504,7 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
       break;
     }
     st = fwd_impl(qc, kc, vc, dtype, 1, hc, N, D, &plans[c], alpha, h0, H, oc, lc, lin_ws, lin_bytes, stream,
-                  kPartAttend);
+                  kPartAttention);
   }
   return st;
 }

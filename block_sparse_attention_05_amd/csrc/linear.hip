@@ -202,7 +202,15 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float *__restr
   if (e >= per) return;
   const float *p = partial + (size_t)bh * chunks * per + e;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += p[(size_t)c * per];
+  int c = 0;
+  for (; c + 8 <= chunks; c += 8) {   // eight loads in flight, added in chunk order
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = p[(size_t)(c + u) * per];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += x[u];
+  }
+  for (; c < chunks; ++c) s += p[(size_t)c * per];
   if (e < D * D)
     h[(size_t)bh * D * D + e] = s;
   else

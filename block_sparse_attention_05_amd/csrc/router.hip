@@ -781,7 +781,11 @@ __global__ __launch_bounds__(256) void balance_order_kernel(const int32_t *__res
     sorted[r] = make_int4(wc, ch_start[c], ch_len[c], 0);
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {
+    // wave 0 runs the greedy pass with every value wave-uniform (chunk records read through
+    // readfirstlane), so its state lives in scalar registers and its steps run on the
+    // scalar unit; lane 0 writes the pieces
+    const int lane = tid;
     int load[8], cap[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
@@ -791,7 +795,8 @@ __global__ __launch_bounds__(256) void balance_order_kernel(const int32_t *__res
     int np = 0;
     int4 next = sorted[0];
     for (int i = 0; i < nch; ++i) {
-      const int4 ch = next;
+      const int4 ch = make_int4(__builtin_amdgcn_readfirstlane(next.x), __builtin_amdgcn_readfirstlane(next.y),
+                                __builtin_amdgcn_readfirstlane(next.z), 0);
       if (i + 1 < nch) next = sorted[i + 1];   // the next chunk's LDS read overlaps this one
       int start = ch.y, len = ch.z;
       while (len > 0) {
@@ -805,9 +810,11 @@ __global__ __launch_bounds__(256) void balance_order_kernel(const int32_t *__res
           }
         }
         const int take = min(len, cap[x]);
-        pc_off[np] = x * q + (q - cap[x]);  // runs fill an XCD's slots in assignment order
-        pc_start[np] = start;
-        pc_len[np] = take;
+        if (lane == 0) {
+          pc_off[np] = x * q + (q - cap[x]);  // runs fill an XCD's slots in assignment order
+          pc_start[np] = start;
+          pc_len[np] = take;
+        }
         ++np;
         // a split chunk's work is shared pro rata (rounded down per row)
         load[x] += take == ch.z ? ch.x : (ch.x / ch.z) * take;
@@ -816,7 +823,7 @@ __global__ __launch_bounds__(256) void balance_order_kernel(const int32_t *__res
         len -= take;
       }
     }
-    n_pieces = np;
+    if (lane == 0) n_pieces = np;
   }
   __syncthreads();
   const int np = n_pieces;
