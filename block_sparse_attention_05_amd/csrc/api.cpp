@@ -140,12 +140,14 @@ size_t sparse_attn_plan_workspace_bytes(int B, int H, int N, int D, int block_q,
 }
 
 namespace {
-// mask_done: NULL, or an event recorded on `stream` once the CSR is written (before the
-// work order), for work that needs the mask but not the order.
+// pooled, masked: NULL, or events recorded on `stream` once the pooling is done and once
+// the CSR is written (before the work order), for work on another stream that should
+// start after the pooling or needs the mask but not the order.
 sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, int N, int D,
                     int block_q, int block_kv, double topk_frac, double top_p,
                     const int32_t *q_order, const int32_t *kv_order, void *workspace, size_t ws_bytes,
-                    sa_plan *out, hipStream_t stream, hipEvent_t mask_done = nullptr) {
+                    sa_plan *out, hipStream_t stream, hipEvent_t pooled = nullptr,
+                    hipEvent_t masked = nullptr) {
   if (q == nullptr || k == nullptr || out == nullptr) return SA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SA_ERR_INVALID_ARG;
   if (!(topk_frac >= 0.0 && topk_frac <= 1.0)) return SA_ERR_INVALID_ARG;
@@ -182,13 +184,14 @@ sa_status plan_impl(const void *q, const void *k, sa_dtype dtype, int B, int H, 
   p.visit = reinterpret_cast<int32_t *>(scores);   // the select kernel's visit lists
   hipError_t e = launch_pool(q, dtype, BH, H, N, D, block_q, q_order, qbar, stream);
   if (e == hipSuccess) e = launch_pool(k, dtype, BH, H, N, D, block_kv, kv_order, kbar, stream);
+  if (e == hipSuccess && pooled != nullptr) e = hipEventRecord(pooled, stream);
   if (e == hipSuccess) e = launch_scores(qbar, kbar, BH, s.nQ, s.nKV, D, c, scores, stream);
   if (e == hipSuccess)
     e = launch_select(scores, (int)s.R, s.nKV, N % block_kv != 0, m_k, p32, p_all, bitmap, nwords, counts,
                       stream);
   if (e == hipSuccess) e = launch_scan(counts, (int)s.R, p.row_ptr, p.nnz, stream);
   if (e == hipSuccess) e = launch_fill(bitmap, nwords, p.row_ptr, (int)s.R, p.col_idx, stream);
-  if (e == hipSuccess && mask_done != nullptr) e = hipEventRecord(mask_done, stream);
+  if (e == hipSuccess && masked != nullptr) e = hipEventRecord(masked, stream);
   if (e == hipSuccess)
     e = launch_row_order(p.row_ptr, (int)s.R, s.nQ, p.row_order, stream);
   if (e != hipSuccess) return SA_ERR_HIP;
@@ -459,11 +462,14 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
   const bool two = aux_stream != stream;
   // Plans go on aux_stream back to back; forwards on `stream`, each after its chunk's plan.
   // Only the first plan is exposed; the others run under the forwards before them.
-  // ev[c]: chunk c's plan done; ev[L.C]: the caller's earlier work; ev[L.C + 1 + c]: chunk
-  // c's CSR written (the linear apply step waits only for that)
+  // ev[c]: chunk c's plan done; ev[L.C]: the caller's earlier work; with the linear branch
+  // ev[L.C + 1 + c]: chunk c's CSR written (its apply step waits only for that) and
+  // ev[2 L.C + 1 + c]: chunk c's pooling done (its prepass starts after it, so that it
+  // shares the chip with the score and select kernels rather than with the pooling, which
+  // heads the critical chain)
   hipEvent_t *ev = nullptr;
   if (two) {
-    ev = pipeline_events(alpha ? 2 * L.C + 1 : L.C + 1);
+    ev = pipeline_events(alpha ? 3 * L.C + 1 : L.C + 1);
     if (ev == nullptr) return SA_ERR_HIP;
     // the plans start after the caller's earlier work on `stream` (inputs written there)
     if (hipEventRecord(ev[L.C], stream) != hipSuccess || hipStreamWaitEvent(aux_stream, ev[L.C], 0) != hipSuccess)
@@ -475,7 +481,8 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
     char *ws = static_cast<char *>(workspace) + c * L.plan_bytes;
     st = plan_impl(chunk(c, static_cast<const char *>(q)), chunk(c, static_cast<const char *>(k)), dtype, 1, hc,
                    N, D, block_q, block_kv, topk_frac, top_p, nullptr, nullptr, ws, L.plan_bytes, &plans[c],
-                   two ? aux_stream : stream, two && alpha ? ev[L.C + 1 + c] : nullptr);
+                   two ? aux_stream : stream, two && alpha ? ev[2 * L.C + 1 + c] : nullptr,
+                   two && alpha ? ev[L.C + 1 + c] : nullptr);
     if (st == SA_OK && two && hipEventRecord(ev[c], aux_stream) != hipSuccess) st = SA_ERR_HIP;
   }
   // With the linear branch, chunk c's prepass (k and v only) goes on `stream` before the
@@ -491,6 +498,10 @@ sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_
     float *lc = lse ? lse + (size_t)c * L.per * N : nullptr;
     const int h0 = (c * L.per) % H;
     if (alpha) {
+      if (two && hipStreamWaitEvent(stream, ev[2 * L.C + 1 + c], 0) != hipSuccess) {
+        st = SA_ERR_HIP;
+        break;
+      }
       st = fwd_impl(qc, kc, vc, dtype, 1, hc, N, D, &plans[c], alpha, h0, H, oc, lc, lin_ws, lin_bytes, stream,
                     kPartPrepass);
       if (st == SA_OK && two && hipStreamWaitEvent(stream, ev[L.C + 1 + c], 0) != hipSuccess) st = SA_ERR_HIP;

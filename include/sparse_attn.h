@@ -200,10 +200,13 @@ size_t sparse_attn_pipelined_workspace_bytes(int B, int H, int N, int D, int blo
  * q, k, v, o, lse, dtype, block sizes, topk_frac and top_p as for sparse_attn_plan and
  * sparse_attn_fwd; n_chunks >= 1 (values above B*H act as B*H).
  * workspace: sparse_attn_pipelined_workspace_bytes bytes, 256-byte aligned.
+ * With the linear branch and two streams, a chunk's prepass starts once its pooling is
+ * done (it then overlaps the score and select kernels) and its apply step waits only for
+ * its CSR, not for the work order.
  * With two streams the call orders them with HIP events that it makes on its first use in
- * a thread (per device, n_chunks + 1 of them, 2 * n_chunks + 1 with the linear branch,
- * whose apply step waits only for its chunk's CSR) and reuses on every later call from
- * that thread; it creates and destroys nothing per call. */
+ * a thread (per device, n_chunks + 1 of them, 3 * n_chunks + 1 with the linear branch)
+ * and reuses on every later call from that thread; it creates and destroys nothing per
+ * call. */
 sa_status sparse_attn_pipelined(const void *q, const void *k, const void *v, sa_dtype dtype,
                                 int B, int H, int N, int D, int block_q, int block_kv,
                                 double topk_frac, double top_p, int n_chunks,
