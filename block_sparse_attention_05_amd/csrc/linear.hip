@@ -256,6 +256,9 @@ __device__ __forceinline__ void wait_stages(int n) {
 #ifndef LIN_SK
 #define LIN_SK 32
 #endif
+#ifndef LIN_NST
+#define LIN_NST 3
+#endif
 
 // One workgroup of four waves per query block (CSR row). The four waves split the
 // (D/32)^2 blocks of the row's running sum H_S[c][d] in a 2x2 grid: wave w takes c-blocks
@@ -266,14 +269,14 @@ __device__ __forceinline__ void wait_stages(int n) {
 // At the end the waves round H_C^T to bf16, stage it in LDS and write it out in row order
 // with z_C; the forward's epilogue multiplies it by phi(q).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LIN_NST == 3 ? 3 : 2)))
 void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   constexpr int NW = 4;
   constexpr int VROWB = D * 2;              // bytes per tile row (unpadded)
   constexpr int TB = kTile * VROWB;         // bytes per tile
   constexpr int SK = D == 128 ? LIN_SK : 32; // keys per pipeline stage
   constexpr int SPT = kTile / SK;           // stages per tile
-  constexpr int NST = 2 * SPT;              // stages held in LDS (4 * TB bytes in all)
+  constexpr int NST = LIN_NST;              // stages held in LDS
   constexpr int SB = SK * VROWB;            // bytes per tensor per stage
   constexpr int VNIS = SB / 1024;           // 1 KB direct loads per tensor per stage
   constexpr int VNIWS = VNIS / NW;          // ... per wave
@@ -305,9 +308,9 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
     }
   };
   static_assert(NST <= 8, "stage buffers");
-  __shared__ int tiles[kMaxList];                    // the tile list of this row
+  __shared__ uint16_t tiles[kMaxList];               // the tile list of this row
   __shared__ uint32_t keptbits[kMaxKvBlocks / 32];
-  __shared__ float zs[2 * D];                        // z partials, then z_C
+  static_assert(kMaxKvBlocks <= 65536, "tile indices in 16 bits");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -508,18 +511,21 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
     }
   }
 
-  // z partials: this wave's k-step half, both lane halves
+  float zz[WC];   // this wave's z partials (its k-step half), both lane halves added
 #pragma unroll
-  for (int x = 0; x < WC; ++x) {
-    const float zz = zacc[x] + __shfl_xor(zacc[x], 32);
-    if (hf == 0) zs[dp * D + (cp * WC + x) * 32 + l32] = zz;
-  }
+  for (int x = 0; x < WC; ++x) zz[x] = zacc[x] + __shfl_xor(zacc[x], 32);
   // H_C (H - H_S or H_S) in fp32, rounded once to bf16 below
   __syncthreads();  // every wave is done with the stage buffers
+  // z partials, then z_C, in the stage buffer that H_C^T leaves free
+  static_assert(NST >= 3 && 2 * D * 4 <= 2 * SB, "z partials fit in a stage buffer");
+  float *zs = reinterpret_cast<float *>(bufs(2));
+  if (hf == 0)
+#pragma unroll
+    for (int x = 0; x < WC; ++x) zs[dp * D + (cp * WC + x) * 32 + l32] = zz[x];
   // staged H_C^T: row d in the stage buffers (2 * SK rows each), 16-byte granule c/8 at
   // physical granule (c/8) ^ (d mod HG)
   constexpr int RPB = 2 * SK;
-  static_assert(D % RPB == 0 && D / RPB <= NST, "H_C^T fits in the stage buffers");
+  static_assert(D % RPB == 0 && D / RPB <= 2, "H_C^T fits in stage buffers 0 and 1");
 #pragma unroll
   for (int x = 0; x < WC; ++x)
 #pragma unroll
