@@ -1,0 +1,43 @@
+"""The library's host code built with AddressSanitizer (host side only: device code is
+built as usual) and driven through every C-ABI validation path by tests/host_checks.cpp,
+with host arrays at their exact sizes. CPU only: no call in the driver reaches the HIP
+runtime. A report from the sanitizer, or a wrong status code, fails the test."""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+from block_sparse_attention_05_amd import build as B  # noqa: E402
+
+# host-side sanitizer only (device code gets no sanitizer flags)
+ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _run(cmd, **kw):
+    r = subprocess.run(cmd, capture_output=True, text=True, **kw)
+    assert r.returncode == 0, " ".join(cmd) + "\n" + r.stdout[-3000:] + r.stderr[-3000:]
+    return r
+
+
+@pytest.mark.skipif(not os.path.exists(B.HIPCC), reason="hipcc not available")
+def test_host_code_under_address_sanitizer(tmp_path):
+    def comp(kv):
+        src, extra = kv
+        obj = str(tmp_path / (os.path.splitext(src)[0] + ".o"))
+        _run([B.HIPCC] + B.COMMON + extra + ASAN + ["-c", os.path.join(B.CSRC, src), "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(min(8, len(B.SOURCES))) as ex:
+        objs = list(ex.map(comp, B.SOURCES.items()))
+    driver = str(tmp_path / "host_checks.o")
+    _run([B.HIPCC, "-O1", "-std=c++17"] + ASAN + ["-c", os.path.join(ROOT, "tests", "host_checks.cpp"), "-o", driver])
+    exe = str(tmp_path / "host_checks")
+    _run([B.HIPCC, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-o", exe, driver] + objs)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and "host checks passed" in r.stdout, r.stdout + r.stderr[-4000:]
+    assert "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
