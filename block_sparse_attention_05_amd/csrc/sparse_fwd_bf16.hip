@@ -376,6 +376,11 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   constexpr int HG = D / 8;                   // 16-byte granules per H_C^T row
   constexpr int HLW = (D * D / 512) / NW;     // 1 KB loads per wave
   static_assert((D * D / 512) % NW == 0 && D * D / 512 <= 2 * HG, "H_C^T fits in a K/V buffer pair");
+  // With them, one more 1 KB direct load (wave 0) brings the row's z_C and the head's alpha
+  // into the K buffer past the H_C^T rows (at EXO: z_C, then alpha), so the epilogue makes
+  // no global round trip of its own.
+  constexpr int EXO = D == 128 ? 64 * VROWB : 0;
+  static_assert(EXO + 1024 <= kBk * ROWB, "z_C and alpha fit in the K buffer");
   auto issue_hct = [&](char *kd, char *vd) {
     const char *hb = reinterpret_cast<const char *>(a.hct + (size_t)row * D * D);
 #pragma unroll
@@ -386,6 +391,13 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       const uint32_t off = (r * D + (pg ^ (r & (HG - 1))) * 8) * 2;
       char *dst = i < HG ? vd + i * 1024 : kd + (i - HG) * 1024;
       __builtin_amdgcn_global_load_lds((gvoid_t *)(hb + off), (lvoid_t *)dst, 16, 0, 0);
+    }
+    if (wid == 0) {
+      // lanes 0 .. D/4-1: z_C, then D/4 lanes of alpha; lanes past 2*(D/4) repeat them
+      const int idx = lane % (D / 2);
+      const float *src = idx < D / 4 ? a.zc + (size_t)row * D + idx * 4
+                                     : a.alpha + (size_t)((a.alpha_h0 + bh) % a.alpha_H) * D + (idx - D / 4) * 4;
+      __builtin_amdgcn_global_load_lds((gvoid_t *)src, (lvoid_t *)(kd + EXO), 16, 0, 0);
     }
   };
   if (LIN ? n > 0 : true) {
@@ -473,8 +485,6 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   // S^T = K Q^T; H_C^T rows are the A operand.
   float inv_l = 0.0f;
   if (lin_on) {
-    const float *zc = a.zc + (size_t)row * D;
-    float zdot = 0.0f;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       uint4 w = __builtin_bit_cast(uint4, qf[s]);
@@ -483,6 +493,14 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       w.z = phi2(w.z);
       w.w = phi2(w.w);
       qf[s] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    const float *zc = reinterpret_cast<const float *>(((n & 1) ? k1s : k0s) + EXO);   // z_C
+    float zdot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const uint4 w = __builtin_bit_cast(uint4, qf[s]);
       const float4 z0 = *reinterpret_cast<const float4 *>(zc + s * 16 + hf * 8);
       const float4 z1 = *reinterpret_cast<const float4 *>(zc + s * 16 + hf * 8 + 4);
       zdot += bf_lo(w.x) * z0.x + bf_hi(w.x) * z0.y + bf_lo(w.y) * z0.z + bf_hi(w.y) * z0.w +
@@ -490,8 +508,6 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     }
     const float den = zdot + __shfl_xor(zdot, 32);
     inv_l = den > 0.0f ? 1.0f / den : 0.0f;
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
   }
   const char *hv = (n & 1) ? v1s : v0s;   // H_C^T rows 0..63
   const char *hk = (n & 1) ? k1s : k0s;   // H_C^T rows 64..
@@ -514,8 +530,11 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = t * 32 + g * 8 + hf * 4;
-        // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel)
-        const float4 al = *reinterpret_cast<const float4 *>(a.alpha + (size_t)((a.alpha_h0 + bh) % a.alpha_H) * D + d);
+        // O = alpha * Os + (1 - alpha) * Ol, alpha per (head, channel): from LDS when the
+        // linear branch's loads brought it, from memory on a row that keeps every block
+        const float4 al = lin_on
+            ? *reinterpret_cast<const float4 *>(hk + EXO + D * 4 + d * 4)
+            : *reinterpret_cast<const float4 *>(a.alpha + (size_t)((a.alpha_h0 + bh) % a.alpha_H) * D + d);
         const float o0 = al.x * (oacc[t][g * 4 + 0] * inv) + (1.f - al.x) * (lacc[g * 4 + 0] * inv_l);
         const float o1 = al.y * (oacc[t][g * 4 + 1] * inv) + (1.f - al.y) * (lacc[g * 4 + 1] * inv_l);
         const float o2 = al.z * (oacc[t][g * 4 + 2] * inv) + (1.f - al.z) * (lacc[g * 4 + 2] * inv_l);
