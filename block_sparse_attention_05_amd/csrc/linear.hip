@@ -121,20 +121,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void l
 #pragma unroll
   for (int i = 0; i < 8; ++i) zp[i] = 0.0f;
 
+  // The next tile's raw rows are loaded while this tile's MFMAs run (tokens past the end
+  // read as zeros: they contribute nothing, and their phi(k) pad rows are written as 0).
+  uint4 kn[4], vn[4];
+  auto load_rows = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = t0 + rg * 4 + r;
+      kn[r] = make_uint4(0, 0, 0, 0);
+      vn[r] = make_uint4(0, 0, 0, 0);
+      if (stager && tok < t_end) {
+        kn[r] = *reinterpret_cast<const uint4 *>(kg + (size_t)tok * D + col);
+        vn[r] = *reinterpret_cast<const uint4 *>(vg + (size_t)tok * D + col);
+      }
+    }
+  };
+  load_rows(t_beg);
   for (int t0 = t_beg; t0 < t_end; t0 += kTile) {
+    uint4 kr[4], vr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kr[r] = kn[r];
+      vr[r] = vn[r];
+    }
+    if (t0 + kTile < t_end) load_rows(t0 + kTile);
     __syncthreads();
     if (stager) {
-      uint4 kr[4], vr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = t0 + rg * 4 + r;
-        if (tok < t_end) {
-          kr[r] = phi8(*reinterpret_cast<const uint4 *>(kg + (size_t)tok * D + col));
-          vr[r] = *reinterpret_cast<const uint4 *>(vg + (size_t)tok * D + col);
-        } else {
-          kr[r] = make_uint4(0, 0, 0, 0);  // tokens past the end contribute nothing
-          vr[r] = make_uint4(0, 0, 0, 0);
-        }
+        if (tok < t_end) kr[r] = phi8(kr[r]);
         // t0 + 64 <= n_pad, so the pad rows past N are written here as zeros
         *reinterpret_cast<uint4 *>(pk + (size_t)tok * D + col) = kr[r];
         zp[0] += bf(kr[r].x, 0); zp[1] += bf(kr[r].x, 1);
