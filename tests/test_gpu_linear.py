@@ -164,3 +164,33 @@ def test_linear_tile_counts(D, tail):
     ol = linear_branch(ent["q32"], ent["k32"], W.to_f32(vb), rp, ci, w.block_q, w.block_kv)
     mx, rr = check_out(o, ol, "bf16", w.name + " Ol")
     log(f"{w.name}: Ol max|d| {mx:.2e} rel-RMS {rr:.2e}")
+
+
+def test_linear_at_the_kv_block_limit():
+    """4096 KV blocks (N = 262,144, one head): rows whose tile lists reach the apply step's
+    capacity of nKV / 2 entries in both modes (2,048 kept tiles subtracted; 2,049 kept, so
+    2,047 complement tiles summed), a row that sums 1,096 complement tiles, and rows that
+    keep one block; Ol (alpha = 0) on those rows against the oracle's explicit form."""
+    w = W.Workload("lin_max_kv", 1, 1, 64, (64, 64, 64), "bf16", 128, 64, 0.01, 0.85, 16, linear=True, seed=4)
+    assert w.n_kvblk == 4096 and w.n_qblk == 2048
+    ent = inputs(w)
+    vb, dv = offset_v(ent, 0.5)
+    nq, nkv = w.n_qblk, w.n_kvblk
+    rng = np.random.default_rng(31)
+    keep_counts = {0: 2048, 1: 2049, 2: 3000}
+    rows = []
+    for r in range(nq):
+        c = keep_counts.get(r, 1)
+        rows.append(np.sort(rng.choice(nkv, c, replace=False)))
+    rp = np.zeros(nq + 1, np.int64)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    ci = np.concatenate(rows).astype(np.int32)
+    p = sa.plan_from_csr(ent["dq"], rp, ci, w.block_q, w.block_kv)
+    a0 = torch.zeros((w.H, w.D), dtype=torch.float32, device="cuda")
+    o = sa.fwd(ent["dq"], ent["dk"], dv, p, alpha=a0)
+    check = [(0, 0, 0), (0, 0, 1), (0, 0, 2), (0, 0, 3), (0, 0, nq - 1)]
+    ol = linear_branch(ent["q32"], ent["k32"], W.to_f32(vb), rp, ci, w.block_q, w.block_kv, rows=check)
+    got = np.concatenate([to_f64(o[0, 0, I * 128:min(w.N, (I + 1) * 128)]) for (_, _, I) in check])
+    want = np.concatenate([ol[r] for r in check])
+    mx, rr = check_out(got, want, "bf16", w.name + " Ol")
+    log(f"{w.name}: Ol on rows with 2,048 / 2,049 / 3,000 / 1 kept blocks max|d| {mx:.2e} rel-RMS {rr:.2e}")
