@@ -287,6 +287,7 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wid >= 0 && wid < NW);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -358,15 +359,22 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
   const int32_t *__restrict__ cols = a.visit ? a.visit + (size_t)row * a.n_kvblk : a.col_idx + beg;
 
+  // Buffer resources over this head's K (N * D bytes) and V^T (whole blocks): lane
+  // offsets go in the VGPR offset and the tile's byte offset in the scalar one, so an
+  // issue costs no per-lane address arithmetic. Both spans are at most 32 MiB (4096 blocks
+  // of 64 keys at D = 128), and every offset used is inside them.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kg, (short)0, N * D, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)vtg, (short)0, a.n_kvblk * TB, kRawBufferWord3);
   auto issue = [&](int J, char *kdst, char *vdst) {
     const uint8_t *kb = kg + (size_t)J * kBk * D;
-    const uint8_t *vb = vtg + (size_t)J * TB;
+    const int toff = J * TB;
     if (J != ragged_blk) {
 #pragma unroll
       for (int m = 0; m < NIW; ++m) {
         const int i = wid + m * NW;
         if (i < NI)
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + koffs[m]), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lvoid_t *)(kdst + i * 1024), 16, (int)koffs[m], toff, 0, 0);
       }
     } else {
       // K rows past N reload the last valid row (in bounds, finite); V^T is stored
@@ -387,7 +395,7 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
     for (int m = 0; m < NIW; ++m) {
       const int i = wid + m * NW;
       if (i < NI)
-        __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + voffs[m]), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lvoid_t *)(vdst + i * 1024), 16, (int)voffs[m], toff, 0, 0);
     }
   };
 

@@ -10,6 +10,9 @@ namespace sa {
 
 constexpr int kMaxKvBlocks = 4096;
 constexpr size_t kAlign = 256;
+// Word 3 of a raw buffer resource on CDNA: 32-bit data format (field bits 15..18 = 4),
+// no swizzle, no thread-id add. Offsets are bytes (stride 0).
+constexpr int kRawBufferWord3 = 0x00020000;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

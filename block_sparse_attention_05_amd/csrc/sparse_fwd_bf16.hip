@@ -18,7 +18,8 @@
 //                    LSE is written the max is exact (margin 0) and the largest term of
 //                    every row sum is exactly 1;
 //   O^T += V^T P^T   bf16 MFMA; P packed with v_cvt_pk_bf16_f32.
-// K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4), row-major with
+// K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds for whole
+// tiles, global_load_lds_dwordx4 for the ragged and gathered ones), row-major with
 // one pad granule per row, double-buffered: the next tile's loads are in flight while the
 // current tile is computed, with one barrier per tile. The V^T operand is read with the
 // transposing LDS read ds_read_b64_tr_b16, so V needs no transposition on the way in. The
@@ -104,6 +105,7 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
+  __builtin_assume(wid >= 0 && wid < NW);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -206,22 +208,31 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
+  // Full tiles load through buffer resources over this head's K and V: the lane offset
+  // is the VGPR offset and the tile's byte offset the scalar one, so an issue costs no
+  // per-lane address arithmetic. A head holds N * D * 2 bytes (at most 4096 blocks of 64
+  // keys: 64 MiB at D = 128); the range check only guards, every full-tile offset is
+  // inside it.
+  const int head_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kg, (short)0, head_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vg, (short)0, head_bytes, kRawBufferWord3);
   auto issue = [&](int J, char *kdst, char *vdst) {
     const int j0 = J * kBk;
     const char *kb = reinterpret_cast<const char *>(kg + (size_t)j0 * D);
     const char *vb = reinterpret_cast<const char *>(vg + (size_t)j0 * D);
     if (J != ragged_blk) {
+      const int toff = j0 * D * 2;
 #pragma unroll
       for (int m = 0; m < NIW; ++m) {
         const int i = wid + m * NW;
         if (i < NI)
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lvoid_t *)(kdst + i * 1024), 16, (int)goff[m], toff, 0, 0);
       }
 #pragma unroll
       for (int m = 0; m < VNIW; ++m) {
         const int i = wid + m * NW;
         if (i < VNI)
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + vgoff[m]), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lvoid_t *)(vdst + i * 1024), 16, (int)vgoff[m], toff, 0, 0);
       }
     } else {
       // the ragged last block: rows past N reload the last valid row (in bounds, finite)
