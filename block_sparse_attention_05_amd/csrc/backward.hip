@@ -190,8 +190,26 @@ void bwd_dq_kernel(BwdArgs a) {
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
   const int32_t *__restrict__ cols = a.col_idx + beg;
 
+  // Full tiles load through buffer resources over this head's K and V (N * D * 2 bytes,
+  // at most 64 MiB): the lane offset is the VGPR offset and the tile's byte offset the
+  // scalar one, so an issue costs no per-lane address arithmetic. Every offset used is
+  // inside the head; the ragged last block keeps its clamped global loads.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kg, (short)0, N * D * 2, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vg, (short)0, N * D * 2, kRawBufferWord3);
   auto issue = [&](int J, char *kdst, char *vdst) {
     const int j0 = J * kBk;
+    if (J != ragged_blk) {
+      const int toff = j0 * D * 2;
+#pragma unroll
+      for (int m = 0; m < NIW; ++m) {
+        const int i = wid + m * NW;
+        if (i < NI) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lvoid_t *)(kdst + i * 1024), 16, (int)goff[m], toff, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lvoid_t *)(vdst + i * 1024), 16, (int)goff[m], toff, 0, 0);
+        }
+      }
+      return;
+    }
     const char *kb = reinterpret_cast<const char *>(kg + (size_t)j0 * D);
     const char *vb = reinterpret_cast<const char *>(vg + (size_t)j0 * D);
     const int last = N - 1 - j0;
@@ -199,13 +217,9 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int m = 0; m < NIW; ++m) {
       const int i = wid + m * NW;
       if (i < NI) {
-        uint32_t off = goff[m];
-        if (J == ragged_blk) {
-          // rows past N reload the last valid row (in bounds, finite; masked below)
-          const int p = 64 * i + lane;
-          const int c = p % GR;
-          off = (min(p / GR, last) * D + (c < D / 8 ? c : 0) * 8) * 2;
-        }
+        const int p = 64 * i + lane;
+        const int c = p % GR;
+        const uint32_t off = (min(p / GR, last) * D + (c < D / 8 ? c : 0) * 8) * 2;
         __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + off), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + off), (lvoid_t *)(vdst + i * 1024), 16, 0, 0);
       }
@@ -392,16 +406,20 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int lv = lane & 15;
   const float *ldsrc = (lv < 8 ? lse2g : dvg) + 4 * (lv & 7);
 
+  // whole stages load through buffer resources over this head's Q and dO (N * D * 2
+  // bytes), with the stage's byte offset as the scalar offset; every offset used is
+  // inside the head
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void *)qg, (short)0, N * D * 2, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void *)dog, (short)0, N * D * 2, kRawBufferWord3);
   auto issue = [&](int q0, char *buf) {
-    const char *qb = reinterpret_cast<const char *>(qg + (size_t)q0 * D);
-    const char *db = reinterpret_cast<const char *>(dog + (size_t)q0 * D);
     if (q0 + SR <= N) {
+      const int soff = q0 * D * 2;
 #pragma unroll
       for (int m = 0; m < NIQW; ++m) {
         const int i = wid + m * NW;
         if (i < NIQ) {
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(qb + toffs[m]), (lvoid_t *)(buf + i * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(db + toffs[m]), (lvoid_t *)(buf + TILEB + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lvoid_t *)(buf + i * 1024), 16, (int)toffs[m], soff, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lvoid_t *)(buf + TILEB + i * 1024), 16, (int)toffs[m], soff, 0, 0);
         }
       }
     } else {
