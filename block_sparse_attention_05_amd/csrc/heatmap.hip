@@ -93,14 +93,19 @@ __global__ __launch_bounds__(64 * NW) void tile_stats_bf16_kernel(const uint16_t
     goff[m] = ((p / GR) * D + (c < D / 8 ? c : 0) * 8) * 2;
   }
   const int ragged_blk = (N % kBk) ? (N / kBk) : -1;
+  // whole tiles load through a buffer resource over this head's K (N * D * 2 bytes, at
+  // most 64 MiB) with the tile's byte offset as the scalar offset; every offset used is
+  // inside the head
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kg, (short)0, N * D * 2, kRawBufferWord3);
   auto issue = [&](int J, char *kdst) {
     const char *kb = reinterpret_cast<const char *>(kg + (size_t)J * kBk * D);
     if (J != ragged_blk) {
+      const int toff = J * kBk * D * 2;
 #pragma unroll
       for (int m = 0; m < NIW; ++m) {
         const int i = wid + m * NW;
         if (i < NI)
-          __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lvoid_t *)(kdst + i * 1024), 16, (int)goff[m], toff, 0, 0);
       }
     } else {
       // rows past N reload the last valid row (in bounds, finite; masked below)

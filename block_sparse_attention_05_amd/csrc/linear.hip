@@ -408,23 +408,31 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   }
   const int ragged_blk = (N % kTile) ? (N / kTile) : -1;
 
+  // Buffer resources over this head's phi(K) rows (n_pad * D * 2 bytes) and V rows
+  // (N * D * 2 bytes), both at most 64 MiB: a stage's byte offset goes in the scalar
+  // offset and the lane's offset in the VGPR one, so an issue costs no per-lane address
+  // arithmetic. Every offset used is inside the head.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)pk, (short)0, lb.n_pad * D * 2, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vg, (short)0, N * D * 2, kRawBufferWord3);
+
   // stage st: keys r0 .. r0 + SK - 1 of tile tiles[st / SPT], r0 = SK * (st % SPT)
   auto issue = [&](int st, char *buf) {
     const int J = tiles[st / SPT];
     const int r0 = SK * (st % SPT);
     char *kdst = buf;
     char *vdst = buf + SB;
-    const char *kb = reinterpret_cast<const char *>(pk + ((size_t)J * kTile + r0) * D);
-    const char *vb = reinterpret_cast<const char *>(vg + ((size_t)J * kTile + r0) * D);
+    const int soff = (J * kTile + r0) * D * 2;
     // phi(K) rows past N are zero pad rows of the prepass buffer
 #pragma unroll
     for (int m = 0; m < VNIWS; ++m)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(kb + goff[m]), (lvoid_t *)(kdst + (wid + m * NW) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lvoid_t *)(kdst + (wid + m * NW) * 1024), 16, (int)goff[m], soff, 0, 0);
     if (J != ragged_blk) {
 #pragma unroll
       for (int m = 0; m < VNIWS; ++m)
-        __builtin_amdgcn_global_load_lds((gvoid_t *)(vb + goff[m]), (lvoid_t *)(vdst + (wid + m * NW) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lvoid_t *)(vdst + (wid + m * NW) * 1024), 16, (int)goff[m], soff, 0, 0);
     } else {
+      const char *vb = reinterpret_cast<const char *>(vg + ((size_t)J * kTile + r0) * D);
       // V rows past N reload the last valid row (finite; their phi(k) is zero)
       const int last = N - 1 - J * kTile - r0;   // may be negative: the whole stage is past N
 #pragma unroll
