@@ -11,7 +11,8 @@
 // output is deterministic.
 //
 // One workgroup per row, one wave per 32 queries. K tiles go from HBM straight into LDS
-// (global_load_lds_dwordx4), padded by one 16-byte granule per row, double-buffered with
+// (buffer_load_dwordx4 ... lds for whole tiles, global_load_lds_dwordx4 for the ragged
+// last one), padded by one 16-byte granule per row, double-buffered with
 // one barrier per tile, as in the forward kernel. Each wave's per-tile partials go to a
 // 128-slot LDS ring; wave 0 folds a group of 64 tiles into the outputs while the next
 // group runs.
