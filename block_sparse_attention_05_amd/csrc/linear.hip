@@ -343,10 +343,11 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   const uint16_t *vg = reinterpret_cast<const uint16_t *>(a.v) + head;
   const uint16_t *pk = lb.phik + (size_t)bh * lb.n_pad * D;
 
-  // The accumulators start from the head's total H when the kept tiles are subtracted
-  // (their phi(K) operands then enter negated, an exact sign flip), so H_C = H - H_S forms
-  // in fp32 inside the MFMA chain. H is read before the row's CSR range is known, so its
-  // loads overlap that round trip; rows that sum the complement drop it.
+  // The accumulators start from -H when the kept tiles are subtracted, so -H + H_S forms
+  // in fp32 inside the MFMA chain and H_C is its negation (exact: round-to-nearest is
+  // symmetric in sign, so this is bit for bit H - H_S with every operand negated), taken
+  // once at the end. H is read before the row's CSR range is known, so its loads overlap
+  // that round trip; rows that sum the complement drop it.
   const float *hg = lb.h + (size_t)bh * D * D;
   floatx16 hacc[WC][WD];
 #pragma unroll
@@ -461,8 +462,7 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
 #pragma unroll
     for (int y = 0; y < WD; ++y)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) hacc[x][y][i] = subtract ? hacc[x][y][i] : 0.0f;
-  const uint32_t neg = subtract ? 0x80008000u : 0u;
+      for (int i = 0; i < 16; ++i) hacc[x][y][i] = subtract ? -hacc[x][y][i] : 0.0f;
   float zacc[WC];
 #pragma unroll
   for (int x = 0; x < WC; ++x) zacc[x] = 0.0f;
@@ -503,17 +503,10 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
           }
       }
 #pragma unroll
-      for (int x = 0; x < WC; ++x) {
-        uint4 w = __builtin_bit_cast(uint4, av[x]);
-        w.x ^= neg;
-        w.y ^= neg;
-        w.z ^= neg;
-        w.w ^= neg;
-        const bf16x8_t an = __builtin_bit_cast(bf16x8_t, w);
+      for (int x = 0; x < WC; ++x)
 #pragma unroll
         for (int y = 0; y < WD; ++y)
-          hacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(an, bv[y], hacc[x][y], 0, 0, 0);
-      }
+          hacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], hacc[x][y], 0, 0, 0);
     }
   };
 
@@ -538,7 +531,8 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
   float zz[WC];   // this wave's z partials (its k-step half), both lane halves added
 #pragma unroll
   for (int x = 0; x < WC; ++x) zz[x] = zacc[x] + __shfl_xor(zacc[x], 32);
-  // H_C (H - H_S or H_S) in fp32, rounded once to bf16 below
+  // H_C (-(-H + H_S) or H_S) in fp32, rounded once to bf16 below
+  const float hsign = subtract ? -1.0f : 1.0f;
   __syncthreads();  // every wave is done with the stage buffers
   // z partials, then z_C, in the stage buffer that H_C^T leaves free
   static_assert(NST >= 3 && 2 * D * 4 <= 2 * SB, "z partials fit in a stage buffer");
@@ -560,7 +554,8 @@ void linear_apply_kernel(FwdArgs a, LinearBufs lb) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int gr = (cp * WC + x) * 4 + q4;
         *reinterpret_cast<uint2 *>(hrow + ((gr ^ (d & (HG - 1))) * 16) + hf * 8) =
-            pack4(hacc[x][y][q4 * 4 + 0], hacc[x][y][q4 * 4 + 1], hacc[x][y][q4 * 4 + 2], hacc[x][y][q4 * 4 + 3]);
+            pack4(hsign * hacc[x][y][q4 * 4 + 0], hsign * hacc[x][y][q4 * 4 + 1], hsign * hacc[x][y][q4 * 4 + 2],
+                  hsign * hacc[x][y][q4 * 4 + 3]);
       }
     }
   __syncthreads();
