@@ -475,6 +475,35 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if constexpr (!LIN) {
     const float inv = 1.0f / l_tot;
+    if (a.q_order == nullptr) {
+      // Output rows are contiguous: the wave stages its 32 x D bf16 block in the K/V
+      // buffer that the row's last tile left free (no loads go there: the last tile issues
+      // none), with 16-byte granule c of row r at c ^ (r mod D/8), then writes it out in
+      // whole rows, 1 KB per store instruction instead of 16-byte pieces of 32 rows.
+      constexpr int GPR = D / 8;               // 16-byte granules per output row
+      constexpr int RPI = 64 / GPR;            // rows per store instruction
+      char *fb = (n & 1) ? ((wid & 2) ? v1s : k1s) : ((wid & 2) ? v0s : k0s);
+      char *ob = fb + (wid & 1) * (32 * D * 2);
+      static_assert(2 * 32 * D * 2 <= kBk * VROWB, "two waves' output blocks fit in a V buffer");
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = t * 4 + g;
+          *reinterpret_cast<uint2 *>(ob + l32 * (D * 2) + ((c ^ (l32 & (GPR - 1))) * 16) + hf * 8) =
+              pack4(oacc[t][g * 4 + 0] * inv, oacc[t][g * 4 + 1] * inv, oacc[t][g * 4 + 2] * inv,
+                    oacc[t][g * 4 + 3] * inv);
+        }
+      const int q0 = I * BQ + wid * 32;        // first query row of this wave
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / GPR, c = lane % GPR;
+        const uint4 w = *reinterpret_cast<const uint4 *>(ob + r * (D * 2) + ((c ^ (r & (GPR - 1))) * 16));
+        if (q0 + r < N) *reinterpret_cast<uint4 *>(og + (size_t)(q0 + r) * D + c * 8) = w;
+      }
+      if (q_ok && a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      return;
+    }
     if (q_ok) {
       uint16_t *orow = og + (size_t)qrow * D;
 #pragma unroll
