@@ -552,6 +552,14 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
   const char *hv = (n & 1) ? v1s : v0s;   // H_C^T rows 0..63
   const char *hk = (n & 1) ? k1s : k0s;   // H_C^T rows 64..
   uint16_t *orow = og + (size_t)qrow * D;
+  // With contiguous output rows the blended block is staged as in the plain epilogue, in
+  // the last tile's K/V buffer: free once every wave has passed the barrier above (with
+  // the linear branch) or, without it, the buffer that the last tile left unused.
+  constexpr int GPR = D / 8;
+  constexpr int RPI = 64 / GPR;
+  const bool staged = a.q_order == nullptr;
+  const int fbi = lin_on ? ((n - 1) & 1) : (n & 1);
+  char *ob = (fbi ? ((wid & 2) ? v1s : k1s) : ((wid & 2) ? v0s : k0s)) + (wid & 1) * (32 * D * 2);
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
     floatx16 lacc;
@@ -579,8 +587,23 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
         const float o1 = al.y * (oacc[t][g * 4 + 1] * inv) + (1.f - al.y) * (lacc[g * 4 + 1] * inv_l);
         const float o2 = al.z * (oacc[t][g * 4 + 2] * inv) + (1.f - al.z) * (lacc[g * 4 + 2] * inv_l);
         const float o3 = al.w * (oacc[t][g * 4 + 3] * inv) + (1.f - al.w) * (lacc[g * 4 + 3] * inv_l);
-        *reinterpret_cast<uint2 *>(orow + d) = pack4(o0, o1, o2, o3);
+        if (staged) {
+          const int c = t * 4 + g;
+          *reinterpret_cast<uint2 *>(ob + l32 * (D * 2) + ((c ^ (l32 & (GPR - 1))) * 16) + hf * 8) =
+              pack4(o0, o1, o2, o3);
+        } else {
+          *reinterpret_cast<uint2 *>(orow + d) = pack4(o0, o1, o2, o3);
+        }
       }
+    }
+  }
+  if (staged) {
+    const int q0 = I * BQ + wid * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / GPR, c = lane % GPR;
+      const uint4 w = *reinterpret_cast<const uint4 *>(ob + r * (D * 2) + ((c ^ (r & (GPR - 1))) * 16));
+      if (q0 + r < N) *reinterpret_cast<uint4 *>(og + (size_t)(q0 + r) * D + c * 8) = w;
     }
   }
   if (q_ok && a.lse && hf == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
