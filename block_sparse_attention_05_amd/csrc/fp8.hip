@@ -582,29 +582,42 @@ void sparse_fwd_fp8_kernel(Fp8FwdArgs a) {
       tile(j_cur, e_cur, k1s, v1s, std::true_type{});
   }
 
-  // epilogue: O[q][d] = acc * 2^ev[d] / l, stored bf16
+  // epilogue: O[q][d] = acc * 2^ev[d] / l, stored bf16. Once every wave is past the last
+  // tile, each wave stages its 32 x D block in a K/V buffer of its own (16-byte granule c
+  // of row r at c ^ (r mod D/8)) and writes it out in whole rows, 1 KB per store
+  // instruction instead of 8-byte pieces of 32 rows.
   const float l_tot = lacc[0];
   const float inv = 1.0f / l_tot;
-  if (q_ok) {
-    uint16_t *orow = og + (size_t)qi * D;
-    const int32_t *veb = a.ve + (size_t)bh * D;
+  constexpr int GPR = D / 8;                 // 16-byte granules per output row
+  constexpr int RPI = 64 / GPR;              // rows per store instruction
+  static_assert(32 * D * 2 <= TB, "a wave's output block fits in one K/V buffer");
+  __syncthreads();
+  char *ob = wid == 0 ? k0s : wid == 1 ? v0s : wid == 2 ? k1s : v1s;
+  const int32_t *veb = a.ve + (size_t)bh * D;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+  for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = t * 32 + g * 8 + hf * 4;
-        const int4 ev = *reinterpret_cast<const int4 *>(veb + d);
-        const __bf16 b0 = (__bf16)ldexpf(oacc[t][g * 4 + 0] * inv, ev.x);
-        const __bf16 b1 = (__bf16)ldexpf(oacc[t][g * 4 + 1] * inv, ev.y);
-        const __bf16 b2 = (__bf16)ldexpf(oacc[t][g * 4 + 2] * inv, ev.z);
-        const __bf16 b3 = (__bf16)ldexpf(oacc[t][g * 4 + 3] * inv, ev.w);
-        uint2 pk;
-        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *reinterpret_cast<uint2 *>(orow + d) = pk;
-      }
-    if (a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot) - poff) * 0.69314718055994531f;
+    for (int g = 0; g < 4; ++g) {
+      const int d = t * 32 + g * 8 + hf * 4;
+      const int4 ev = *reinterpret_cast<const int4 *>(veb + d);
+      const __bf16 b0 = (__bf16)ldexpf(oacc[t][g * 4 + 0] * inv, ev.x);
+      const __bf16 b1 = (__bf16)ldexpf(oacc[t][g * 4 + 1] * inv, ev.y);
+      const __bf16 b2 = (__bf16)ldexpf(oacc[t][g * 4 + 2] * inv, ev.z);
+      const __bf16 b3 = (__bf16)ldexpf(oacc[t][g * 4 + 3] * inv, ev.w);
+      uint2 pk;
+      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+      const int c = t * 4 + g;
+      *reinterpret_cast<uint2 *>(ob + l32 * (D * 2) + ((c ^ (l32 & (GPR - 1))) * 16) + hf * 8) = pk;
+    }
+  const int q0 = I * BQ + wid * 32;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / GPR, c = lane % GPR;
+    const uint4 w = *reinterpret_cast<const uint4 *>(ob + r * (D * 2) + ((c ^ (r & (GPR - 1))) * 16));
+    if (q0 + r < N) *reinterpret_cast<uint4 *>(og + (size_t)(q0 + r) * D + c * 8) = w;
   }
+  if (q_ok && a.lse && hf == 0) a.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot) - poff) * 0.69314718055994531f;
 }
 
 template <int D, bool I8>
