@@ -320,17 +320,31 @@ void bwd_dq_kernel(BwdArgs a) {
       tile(cols[n - 1], k1s, v1s, std::true_type{});
   }
 
-  if (q_ok) {
+  // dQ out: each wave stages its 32 x D block in the K/V buffer pair that the row's last
+  // tile left free (no loads go there), 16-byte granule c of row r at c ^ (r mod D/8),
+  // and writes it in whole rows, 1 KB per store instruction
+  {
+    constexpr int GPR = D / 8;
+    constexpr int RPI = 64 / GPR;
+    static_assert(2 * 32 * D * 2 <= kBk * ROWB, "two waves' blocks fit in one buffer");
     const float c = a.scale;
-    uint16_t *orow = dqg + (size_t)qi * D;
+    char *ob = ((n & 1) ? ((wid & 2) ? v1s : k1s) : ((wid & 2) ? v0s : k0s)) + (wid & 1) * (32 * D * 2);
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = t * 32 + g * 8 + hf * 4;
-        *reinterpret_cast<uint2 *>(orow + d) = pack4(dqacc[t][g * 4 + 0] * c, dqacc[t][g * 4 + 1] * c,
-                                                     dqacc[t][g * 4 + 2] * c, dqacc[t][g * 4 + 3] * c);
+        const int gc = t * 4 + g;
+        *reinterpret_cast<uint2 *>(ob + l32 * (D * 2) + ((gc ^ (l32 & (GPR - 1))) * 16) + hf * 8) =
+            pack4(dqacc[t][g * 4 + 0] * c, dqacc[t][g * 4 + 1] * c, dqacc[t][g * 4 + 2] * c,
+                  dqacc[t][g * 4 + 3] * c);
       }
+    const int q0 = I * BQ + wid * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / GPR, gc = lane % GPR;
+      const uint4 w = *reinterpret_cast<const uint4 *>(ob + r * (D * 2) + ((gc ^ (r & (GPR - 1))) * 16));
+      if (q0 + r < N) *reinterpret_cast<uint4 *>(dqg + (size_t)(q0 + r) * D + gc * 8) = w;
+    }
   }
 }
 
@@ -537,20 +551,41 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  if (k_ok) {
+  // dK and dV out: once both waves are done with the stage buffers, each wave stages its
+  // 32 x D blocks of dK and dV there (16-byte granule c of row r at c ^ (r mod D/8)) and
+  // writes them in whole rows, 1 KB per store instruction
+  {
+    constexpr int GPR = D / 8;
+    constexpr int RPI = 64 / GPR;
+    constexpr int BLK = 32 * D * 2;            // one wave's 32 x D bf16 block
+    static_assert(NW * 2 * BLK <= 2 * STAGE, "both waves' dK and dV blocks fit in the stage buffers");
     const float c = a.scale;
-    uint16_t *krow = a.dk + head + (size_t)key * D;
-    uint16_t *vrow = a.dv + head + (size_t)key * D;
+    __syncthreads();
+    char *kb = smem + wid * (2 * BLK);
+    char *vb = kb + BLK;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = t * 32 + g * 8 + hf * 4;
-        *reinterpret_cast<uint2 *>(krow + d) = pack4(dkacc[t][g * 4 + 0] * c, dkacc[t][g * 4 + 1] * c,
+        const int gc = t * 4 + g;
+        const int off = l32 * (D * 2) + ((gc ^ (l32 & (GPR - 1))) * 16) + hf * 8;
+        *reinterpret_cast<uint2 *>(kb + off) = pack4(dkacc[t][g * 4 + 0] * c, dkacc[t][g * 4 + 1] * c,
                                                      dkacc[t][g * 4 + 2] * c, dkacc[t][g * 4 + 3] * c);
-        *reinterpret_cast<uint2 *>(vrow + d) = pack4(dvacc[t][g * 4 + 0], dvacc[t][g * 4 + 1],
+        *reinterpret_cast<uint2 *>(vb + off) = pack4(dvacc[t][g * 4 + 0], dvacc[t][g * 4 + 1],
                                                      dvacc[t][g * 4 + 2], dvacc[t][g * 4 + 3]);
       }
+    const int k0 = J * kBk + wid * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / GPR, gc = lane % GPR;
+      const int off = r * (D * 2) + ((gc ^ (r & (GPR - 1))) * 16);
+      const uint4 wk = *reinterpret_cast<const uint4 *>(kb + off);
+      const uint4 wv = *reinterpret_cast<const uint4 *>(vb + off);
+      if (k0 + r < N) {
+        *reinterpret_cast<uint4 *>(a.dk + head + (size_t)(k0 + r) * D + gc * 8) = wk;
+        *reinterpret_cast<uint4 *>(a.dv + head + (size_t)(k0 + r) * D + gc * 8) = wv;
+      }
+    }
   }
 }
 
