@@ -97,13 +97,17 @@ def mask_quality(tmax: np.ndarray, tmass: np.ndarray, rp: np.ndarray, ci: np.nda
 
 
 def source_hash() -> str:
+    """sha256 (first 16 hex digits) of the forward kernel's source followed by the compile
+    flags the library build gives it: a change to either invalidates recorded counters."""
+    from block_sparse_attention_05_amd import build as _build
+    flags = _build.COMMON + _build.SOURCES[os.path.basename(KERNEL_SRC)]
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        return hashlib.sha256(f.read() + b"\0" + " ".join(flags).encode()).hexdigest()[:16]
 
 
 def traffic_for(workload: str, launch_bytes_alg: float):
     """HBM bytes per forward launch from committed rocprofv3 counters, when they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and compile flags; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
