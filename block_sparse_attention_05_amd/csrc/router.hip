@@ -165,9 +165,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ x, int 
 
 // The same sums for bf16 rows in raster order (no table) with a register footprint of at
 // most 32: two rows in flight per thread and 32-bit byte offsets from one base (tensors
-// under 4 GiB). Two forward workgroups leave 32 registers per lane of a SIMD free, so
-// this kernel's waves fit beside them: the pooling of one chunk of heads runs on the
-// CUs that the previous chunk's forward occupies instead of waiting for them.
+// under 4 GiB). With enough workgroups it matches the wide kernel's bandwidth with a
+// quarter of its registers.
 template <int D>
 __global__ __launch_bounds__(256) void pool_lean_kernel(const uint16_t *__restrict__ x, int N, int bs,
                                                         int nblk, long total_blocks,
@@ -853,7 +852,7 @@ hipError_t launch_pool(const void *x, sa_dtype dt, int BH, int H, int N, int D, 
   // The lean kernel keeps two rows in flight per thread: with fewer than about three
   // workgroups per CU that leaves too few bytes in flight (on the 12-head 32,760-token
   // shape, 192 and 384 workgroups, it takes 30 us a launch against 19), with more it is
-  // as fast as the wide one and also fits beside the forward.
+  // as fast as the wide one.
   constexpr unsigned kLeanMinGrid = 3 * 256;
   const bool lean = order == nullptr && (size_t)BH * N * D * 2 < ((size_t)1 << 32) && grid >= kLeanMinGrid;
   if (dt == SA_BF16 && lean) {
