@@ -68,3 +68,14 @@ def test_traffic_needs_the_profiled_kernel_source(tmp_path, monkeypatch):
     assert bench.traffic_for("other", 1.0) is None
     f.write_text(json.dumps({"w": {"kernel_source_sha256_16": "0" * 16, "hbm_bytes_per_launch": 123}}))
     assert bench.traffic_for("w", 1.0) is None
+
+
+def test_traffic_key_covers_the_compile_flags(monkeypatch):
+    """Counters taken on one build of the forward are not reported for another build of the
+    same source (a changed instruction schedule changes the kernel)."""
+    from block_sparse_attention_05_amd import build as B
+    h = bench.source_hash()
+    flags = dict(B.SOURCES)
+    flags["sparse_fwd_bf16.hip"] = [f for f in flags["sparse_fwd_bf16.hip"] if "sched" not in f and f != "-mllvm"]
+    monkeypatch.setattr(B, "SOURCES", flags)
+    assert bench.source_hash() != h
