@@ -215,23 +215,29 @@ __global__ __launch_bounds__(256) void pool_lean_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------- scores
-// S[bh, I, J] for a 64 x 64 tile per workgroup; each thread owns a 4 x 4 patch and keeps
-// one running sum per output, adding the rounded products in ascending d.
+// S[bh, I, J] for a 64 x 64 tile per workgroup; each thread keeps one running sum per
+// output of a 4 x 4 patch, adding the rounded products in ascending d. Thread (ti, tj)
+// owns query rows 4 ti .. 4 ti + 3 and key columns tj, tj + 16, tj + 32, tj + 48, so a
+// wave owns 16 consecutive query rows and skips its products when all of them lie past
+// nQ. Chunks of 32 channels are staged row-major in LDS by 16-byte copies; the row pitch
+// of 36 floats puts the rows one read touches on distinct banks (4 query rows 4 apart,
+// 16 consecutive key rows).
 constexpr int kSt = 64;    // tile edge
 constexpr int kSd = 32;    // d chunk staged in LDS
-constexpr int kSpad = 68;  // LDS row stride (floats)
+constexpr int kSp = 36;    // LDS row pitch (floats)
 
 __global__ __launch_bounds__(256) void scores_kernel(const float *__restrict__ qbar,
                                                      const float *__restrict__ kbar, int nQ,
                                                      int nKV, int D, float c,
                                                      float *__restrict__ S) {
-  __shared__ __align__(16) float qs[kSd][kSpad];
-  __shared__ __align__(16) float ks[kSd][kSpad];
+  __shared__ __align__(16) float qs[kSt][kSp];
+  __shared__ __align__(16) float ks[kSt][kSp];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * kSt;
   const int j0 = blockIdx.x * kSt;
   const int tid = threadIdx.x;
   const int ti = tid / 16, tj = tid % 16;
+  const bool live = i0 + 16 * (tid >> 6) < nQ;   // wave-uniform: some row of this wave exists
   const float *qb = qbar + (size_t)bh * nQ * D;
   const float *kb = kbar + (size_t)bh * nKV * D;
   float acc[4][4];
@@ -240,25 +246,40 @@ __global__ __launch_bounds__(256) void scores_kernel(const float *__restrict__ q
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
   for (int d0 = 0; d0 < D; d0 += kSd) {
-    for (int e = tid; e < kSt * kSd; e += 256) {
-      const int r = e / kSd, dd = e % kSd;
-      qs[dd][r] = (i0 + r < nQ) ? qb[(size_t)(i0 + r) * D + d0 + dd] : 0.0f;
-      ks[dd][r] = (j0 + r < nKV) ? kb[(size_t)(j0 + r) * D + d0 + dd] : 0.0f;
+    // 64 rows x 8 float4 per matrix: two of each per thread
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int e = tid + 256 * m;
+      const int r = e / (kSd / 4), c4 = e % (kSd / 4);
+      float4 qv = make_float4(0.0f, 0.0f, 0.0f, 0.0f), kv = qv;
+      if (i0 + r < nQ) qv = __ldg(reinterpret_cast<const float4 *>(qb + (size_t)(i0 + r) * D + d0 + c4 * 4));
+      if (j0 + r < nKV) kv = __ldg(reinterpret_cast<const float4 *>(kb + (size_t)(j0 + r) * D + d0 + c4 * 4));
+      *reinterpret_cast<float4 *>(&qs[r][c4 * 4]) = qv;
+      *reinterpret_cast<float4 *>(&ks[r][c4 * 4]) = kv;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < kSd; ++dd) {
-      const float4 qa = *reinterpret_cast<const float4 *>(&qs[dd][ti * 4]);
-      const float4 kv = *reinterpret_cast<const float4 *>(&ks[dd][tj * 4]);
-      const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
-      const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+    if (live) {
+#pragma unroll 2
+      for (int g = 0; g < kSd / 4; ++g) {
+        float qv[4][4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+          const float4 w = *reinterpret_cast<const float4 *>(&qs[ti * 4 + a][g * 4]);
+          qv[a][0] = w.x; qv[a][1] = w.y; qv[a][2] = w.z; qv[a][3] = w.w;
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const float prod = qv[a] * kk[b];
-          acc[a][b] = acc[a][b] + prod;
+          const float4 w = *reinterpret_cast<const float4 *>(&ks[tj + 16 * b][g * 4]);
+          const float kk[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const float prod = qv[a][e] * kk[e];
+              acc[a][b] = acc[a][b] + prod;
+            }
         }
+      }
     }
     __syncthreads();
   }
@@ -269,7 +290,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const float *__restrict__ q
     float *row = S + ((size_t)bh * nQ + I) * nKV;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int J = j0 + tj * 4 + b;
+      const int J = j0 + tj + 16 * b;
       if (J < nKV) row[J] = acc[a][b] * c;
     }
   }
