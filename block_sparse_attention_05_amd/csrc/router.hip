@@ -655,6 +655,10 @@ __global__ __launch_bounds__(256) void select_kernel(float *S, int nKV, int ragg
 }
 
 // ---------------------------------------------------------------- CSR
+// row_ptr = exclusive prefix sum of counts (one workgroup). Each pass covers 1024 * kScanIt
+// rows: a thread loads its kScanIt consecutive counts at once (one memory round trip per
+// pass), sums them in order, and the block scans the thread totals.
+constexpr int kScanIt = 16;
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ counts, int R,
                                                     int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz) {
   __shared__ int wsum[16];
@@ -665,10 +669,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ 
     row_ptr[0] = 0;
   }
   __syncthreads();
-  for (int base = 0; base < R; base += 1024) {
-    const int i = base + tid;
-    const int v = i < R ? counts[i] : 0;
-    int x = v;
+  for (int base = 0; base < R; base += 1024 * kScanIt) {
+    const int i0 = base + tid * kScanIt;
+    int v[kScanIt];
+#pragma unroll
+    for (int u = 0; u < kScanIt; ++u) v[u] = i0 + u < R ? counts[i0 + u] : 0;
+#pragma unroll
+    for (int u = 1; u < kScanIt; ++u) v[u] += v[u - 1];
+    int x = v[kScanIt - 1];   // inclusive scan of the thread totals across the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o);
@@ -686,10 +694,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ 
       if (lane < 16) wsum[lane] = w;
     }
     __syncthreads();
-    const int incl = carry + (wid > 0 ? wsum[wid - 1] : 0) + x;
-    if (i < R) row_ptr[i + 1] = incl;
+    const int before = carry + (wid > 0 ? wsum[wid - 1] : 0) + x - v[kScanIt - 1];
+#pragma unroll
+    for (int u = 0; u < kScanIt; ++u)
+      if (i0 + u < R) row_ptr[i0 + u + 1] = before + v[u];
     __syncthreads();
-    if (tid == 1023) carry = incl;
+    if (tid == 1023) carry = before + v[kScanIt - 1];
     __syncthreads();
   }
   if (tid == 0) *nnz = carry;
