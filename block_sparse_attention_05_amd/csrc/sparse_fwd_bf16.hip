@@ -317,13 +317,13 @@ void sparse_fwd_bf16_kernel(FwdArgs a) {
       const int kt = c >> 1, i0 = (c & 1) * 8;
       float m = sacc[kt][i0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, sacc[kt][i0 + i]);
+      for (int i = 1; i < 8; ++i) m = score_max(m, sacc[kt][i0 + i]);
       mc[c] = m;
     }
-    float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+    float mx = score_max(score_max(mc[0], mc[1]), score_max(mc[2], mc[3]));
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = score_max(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const float mt = mx * sl2;
     const bool need = mt > m_run + lazy;
