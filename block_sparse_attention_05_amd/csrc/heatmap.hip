@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * NW) void tile_stats_bf16_kernel(const uint16_t
       float sm = ring_sum[0][slot];
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
-        mx = fmaxf(mx, ring_max[w][slot]);
+        mx = score_max(mx, ring_max[w][slot]);
         sm = sm + ring_sum[w][slot];
       }
       const size_t o = (size_t)row * n_kvblk + j0 + lane;
@@ -168,14 +168,14 @@ __global__ __launch_bounds__(64 * NW) void tile_stats_bf16_kernel(const uint16_t
       for (int i = 0; i < 16; ++i) {
         const int key = kt * 32 + (i / 4) * 8 + hf * 4 + (i % 4);
         const float p = key < valid ? __builtin_amdgcn_exp2f(sacc[kt][i] * sl2 - lse2) : 0.0f;
-        mx = fmaxf(mx, p);
+        mx = score_max(mx, p);
         sm = sm + p;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = score_max(mx, __shfl_xor(mx, 32));
     sm = sm + __shfl_xor(sm, 32);
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, o));
+      mx = score_max(mx, __shfl_xor(mx, o));
       sm = sm + __shfl_xor(sm, o);
     }
     if (lane == 0) {

@@ -14,11 +14,11 @@ constexpr size_t kAlign = 256;
 // no swizzle, no thread-id add. Offsets are bytes (stride 0).
 constexpr int kRawBufferWord3 = 0x00020000;
 
-// Larger of two scores, for the forward kernels' tile max. fmaxf first quiets any operand
-// the compiler cannot prove canonical (an MFMA result, a lane swap), one VALU instruction
-// each; IEEE maximum (v_maximum3_f32 on gfx950) needs none. The two agree on the scores
-// these kernels see, which are never NaN (a tile max of +0 against -0 only changes the
-// sign of a zero that is then subtracted).
+// Larger of two scores or probabilities, for the attention kernels' tile max. fmaxf first
+// quiets any operand the compiler cannot prove canonical (an MFMA result, a lane swap),
+// one VALU instruction each; IEEE maximum (v_maximum3_f32 on gfx950) needs none. The two
+// agree on the values these kernels see, which are never NaN (a tile max of +0 against -0
+// only changes the sign of a zero that is then subtracted).
 __device__ __forceinline__ float score_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
