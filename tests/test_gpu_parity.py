@@ -147,6 +147,34 @@ def test_fwd_small(case):
     check_out(to_f64(sa.fwd(ent["dq"], ent["dk"], ent["dv"], p)), ref, w.dtype, w.name + " no lse")
 
 
+def test_fwd_signed_zero_queries():
+    """All scores zero: with q = +0 and with q = -0 every kept key gets the same weight, so
+    O is the mean of the kept V rows. The tile max is then +0 or -0, which must not change
+    any output bit, with or without the LSE output."""
+    import torch
+    w = small_workload("ragged_q128", 2, 3, 3000, 128, "bf16", 128, 0.05, 0.9)
+    log(f"fwd signed-zero queries {w.name}")
+    ent = inputs(w)
+    p, (rp, ci) = gpu_plan(w, ent)
+    qpos = torch.zeros_like(ent["dq"])
+    qneg = torch.full(ent["dq"].shape, 0x8000 - 0x10000, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    assert torch.signbit(qneg.float()).all() and not torch.signbit(qpos.float()).any()
+    z32 = np.zeros(ent["q32"].shape, np.float32)
+    ref, rlse = sparse_attention(z32, ent["k32"], W.to_f32(ent["v"]), rp, ci, w.block_q, w.block_kv,
+                                 with_lse=True)
+    outs = []
+    for q in (qpos, qneg):
+        o, lse = sa.fwd(q, ent["dk"], ent["dv"], p, return_lse=True)
+        check_out(to_f64(o), ref, w.dtype, "zero q with lse")
+        assert np.max(np.abs(to_f64(lse) - rlse)) < 2e-3
+        o2 = sa.fwd(q, ent["dk"], ent["dv"], p)
+        check_out(to_f64(o2), ref, w.dtype, "zero q")
+        outs.append((o, lse, o2))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
 def test_plan_nnz_scalar():
     """The plan's device nnz scalar equals row_ptr[R] for the router's plan, the dense
     plan and a caller's CSR."""
